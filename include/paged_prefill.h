@@ -1,0 +1,157 @@
+/*
+ * paged_prefill.h — C ABI of the MI355X (gfx950) paged-KV prefill attention library.
+ *
+ * What the library computes (vLLM PR #54194 report, "Features and motivation"
+ * and "Implementation breakdown"; vLLM PR #50776 report, "Features and
+ * motivation"; vLLM PR #53147 report, "Implementation breakdown"):
+ * for every sequence s of a ragged prefill batch, every query head h and every
+ * new-token row i, the query at absolute position a = ctx_lens[s] + i attends
+ * over the sequence's keys j in [0, L), L = ctx_lens[s] + n_s, where keys
+ * j < ctx_lens[s] are read from a paged KV cache through the block table and
+ * keys j >= ctx_lens[s] are the chunk's new K/V rows.  Scores are
+ * scale * <q, k_j>; a key is allowed when j < L and
+ *   (causal => j <= a) and (window_left >= 0 => j >= a - window_left) and
+ *   (!causal and window_right >= 0 => j <= a + window_right),
+ * or when some multimodal range [st, en] (inclusive, counted only if st < en)
+ * holds both a and j and (window_left >= 0 => j >= a - window_left).
+ * The output row is the softmax-weighted sum of the allowed V rows.
+ * Query head h reads KV head h / (num_heads / num_kv_heads).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates no device memory and keeps no state between calls.  Every call
+ *    is re-entrant and thread-safe.
+ *  - bf16 tensors are passed as raw 16-bit patterns, dense, row-major.
+ *  - Work is enqueued on `stream` (NULL = the default stream) and the call
+ *    returns without synchronising.  A fault during execution surfaces at the
+ *    caller's next synchronisation on that stream.
+ *  - Scalar arguments are checked on the host; device-resident contents
+ *    (lengths, page ids, ranges) are preconditions stated per argument and
+ *    are not checked.  No C++ exception crosses this boundary.
+ *  - Return value: PAGED_PREFILL_OK or one of the negative error codes below.
+ */
+#ifndef PAGED_PREFILL_H
+#define PAGED_PREFILL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+#define PAGED_PREFILL_OK 0
+#define PAGED_PREFILL_ERR_INVALID_ARG (-1) /* a null required pointer or an out-of-range scalar */
+#define PAGED_PREFILL_ERR_UNSUPPORTED (-2) /* head_size not in {64, 128, 256}, or a size this build does not handle */
+#define PAGED_PREFILL_ERR_HIP (-3)         /* the HIP runtime refused the launch */
+
+/*
+ * prefill_attention — one launch of paged-KV prefill attention over a ragged batch.
+ *
+ * Tensors (T = total_q_tokens, H = num_heads, Hkv = num_kv_heads, d = head_size,
+ * P = page_size, S = num_seqs):
+ *   q               bf16 [T][H][d]            queries of the new tokens, sequences packed
+ *   k_new, v_new    bf16 [T][Hkv][d]          the chunk's new keys/values; row query_start_loc[s] + i
+ *                                             is position ctx_lens[s] + i of sequence s.
+ *                                             Both NULL selects the cache-sourced mode: every
+ *                                             position j < L of a sequence is read from the cache
+ *                                             (the new tokens are already written there), as in
+ *                                             the k=None path of vLLM PR #54194 report,
+ *                                             "Implementation breakdown" item 4.
+ *   k_cache, v_cache bf16 [num_pages][P][Hkv][d]  paged cache; position j of sequence s lives in
+ *                                             page block_table[s][j / P], slot j % P.  P may be
+ *                                             any positive size, including non-powers of two
+ *                                             (544, 1040, 1056; vLLM PR #54194 report, "Features
+ *                                             and motivation"): tiles never depend on pages.
+ *   block_table     int32 [S][max_pages_per_seq]; entry p must be a page id in [0, num_pages) for
+ *                   p < cdiv(ctx_lens[s], P) (cdiv(L, P) in cache-sourced mode).  Entries at or
+ *                   beyond that count are NEVER read and may hold anything (e.g. -1); pages not
+ *                   named by a read entry are never touched (vLLM PR #54194 report, "Review
+ *                   highlights": the unmasked block-table load hazard).
+ *   query_start_loc int32 [S+1]; query_start_loc[0] = 0, non-decreasing, query_start_loc[S] = T.
+ *   ctx_lens        int32 [S]; cached tokens per sequence, >= 0.
+ *   mm_ranges       int32 [S][max_mm_ranges][2]; absolute, inclusive [start, end] multimodal
+ *                   ranges (vLLM PR #53147 report, "Key source snippets": [seq][range][start,end]
+ *                   layout, [0, 0] padding, valid only if start < end).  NULL iff max_mm_ranges==0.
+ *   out             bf16 [T][H][d]; written for every new-token row (round-to-nearest-even from
+ *                   fp32).  Must not alias an input.
+ * Scalars:
+ *   window_left     keys j >= a - window_left are allowed; -1 = unbounded.  Inclusive distance,
+ *                   as the windowed-prefill report uses (vLLM PR #50776 report, "Features and
+ *                   motivation"); a width-W window of the multimodal report is W - 1 here.
+ *   window_right    keys j <= a + window_right are allowed when !causal; -1 = unbounded;
+ *                   ignored when causal.
+ *   causal          0 or 1; causal rows sit at their absolute position (bottom-right alignment).
+ *   scale           softmax scale applied to q.k (e.g. 1/sqrt(d)); must be finite and > 0.
+ *   max_q_len       >= every n_s = query_start_loc[s+1] - query_start_loc[s].
+ *   num_pages, max_pages_per_seq, max_mm_ranges  sizes of the tensors above.
+ * Errors: INVALID_ARG for a null required pointer, num_heads % num_kv_heads != 0, non-positive
+ * sizes (page_size, num_heads, num_kv_heads; negative num_seqs/total_q_tokens/max_q_len),
+ * window < -1, causal not 0/1, bad scale, exactly one of k_new/v_new NULL, max_mm_ranges < 0 or
+ * > 4096, max_mm_ranges > 0 with NULL mm_ranges, or a geometry whose positions exceed the
+ * library's 2^24-token limit per sequence; UNSUPPORTED for head_size not in {64, 128, 256};
+ * HIP_ERROR if the launch fails.  An empty batch (num_seqs, total_q_tokens or max_q_len == 0)
+ * returns OK without launching.
+ */
+int prefill_attention(const void* q, const void* k_new, const void* v_new,
+                      const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* query_start_loc,
+                      const int32_t* ctx_lens,
+                      int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                      int32_t page_size, int32_t window_left, int32_t window_right,
+                      int32_t causal, const int32_t* mm_ranges, float scale, void* out,
+                      int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                      int32_t num_pages, int32_t max_pages_per_seq, int32_t max_mm_ranges,
+                      hipStream_t stream);
+
+/*
+ * prefill_attention_validate — the host-side argument checks of prefill_attention, alone.
+ * Takes the same arguments, reads no pointer, launches nothing, needs no GPU.  Returns the
+ * code prefill_attention would return before launching.
+ */
+int prefill_attention_validate(const void* q, const void* k_new, const void* v_new,
+                               const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* query_start_loc,
+                               const int32_t* ctx_lens,
+                               int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                               int32_t page_size, int32_t window_left, int32_t window_right,
+                               int32_t causal, const int32_t* mm_ranges, float scale,
+                               const void* out, int32_t num_seqs, int32_t total_q_tokens,
+                               int32_t max_q_len, int32_t num_pages, int32_t max_pages_per_seq,
+                               int32_t max_mm_ranges);
+
+/*
+ * prefill_attention_tile_config — the tile geometry prefill_attention uses for this head
+ * configuration: *block_q query tokens per Q tile (all heads of a GQA group share a tile) and
+ * *block_n keys per KV tile.  The tile bounds below are expressed in these units.  Host-only.
+ * Errors: INVALID_ARG (null outputs, bad head counts), UNSUPPORTED (head_size).
+ */
+int prefill_attention_tile_config(int32_t head_size, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t* block_q, int32_t* block_n);
+
+/*
+ * prefill_attention_tile_bounds — the KV-tile loop range [lo, hi) of every Q tile, computed on
+ * the GPU by the same device function the attention kernel loops with (the helper-kernel test
+ * pattern of vLLM PR #53147 report, "Key source snippets").  The range unions the base window
+ * with every valid multimodal range that overlaps the tile's query positions, clamps to the
+ * sequence, and converts to tiles of block_n keys (vLLM PR #50776 report, "Key source
+ * snippets"; vLLM PR #53147 report, "Implementation breakdown" item 2).
+ *   bounds_out  device int32 [num_seqs][cdiv(max_q_len, block_q)][2], written (lo, hi); tiles
+ *               past a sequence's last row get (0, 0).
+ * Other arguments as for prefill_attention.  Errors as for prefill_attention.
+ */
+int prefill_attention_tile_bounds(const int32_t* query_start_loc, const int32_t* ctx_lens,
+                                  int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                  int32_t window_left, int32_t window_right, int32_t causal,
+                                  const int32_t* mm_ranges, int32_t num_seqs, int32_t max_q_len,
+                                  int32_t max_mm_ranges, int32_t* bounds_out, hipStream_t stream);
+
+/* prefill_attention_strerror — static description of an error code (never NULL). */
+const char* prefill_attention_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_PREFILL_H */

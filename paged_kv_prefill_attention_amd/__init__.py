@@ -1,0 +1,21 @@
+"""Paged-KV prefill attention for MI355X (gfx950): Python binding of the C ABI.
+
+The computation lives in ``libpagedprefill.so`` (hand-written HIP, built
+in-tree by ``_build.build()``); this package only marshals torch tensors into
+device pointers and streams.
+"""
+
+from ._binding import (  # noqa: F401
+    ERR_HIP,
+    ERR_INVALID_ARG,
+    ERR_UNSUPPORTED,
+    OK,
+    PrefillError,
+    load_library,
+    prefill_attention,
+    strerror,
+    tile_bounds,
+    tile_config,
+    validate,
+)
+from ._build import build, library_path  # noqa: F401

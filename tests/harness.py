@@ -1,0 +1,91 @@
+"""Shared helpers for the GPU tests: move a seeded workload to the device, call
+the HIP library through its binding, and compare with the oracle."""
+
+import numpy as np
+
+import oracle
+from workloads import bf16_bits_to_f32
+
+ATOL = 2e-2
+RTOL = 2e-2
+
+
+def to_device(w, cache_only=False, device="cuda"):
+    import torch
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(
+            torch.bfloat16)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+    return dict(q=bf(w.q), k_new=None if cache_only else bf(w.k_new),
+                v_new=None if cache_only else bf(w.v_new), k_cache=bf(w.k_cache),
+                v_cache=bf(w.v_cache), block_table=i32(w.block_table),
+                query_start_loc=i32(w.query_start_loc), ctx_lens=i32(w.ctx_lens),
+                mm_ranges=None if w.mm_ranges is None else i32(w.mm_ranges))
+
+
+def run_gpu(w, dev=None, cache_only=False, out=None, mm_ranges="default"):
+    import paged_kv_prefill_attention_amd as ppa
+    if dev is None:
+        dev = to_device(w, cache_only=cache_only)
+    mm = dev["mm_ranges"] if isinstance(mm_ranges, str) else mm_ranges
+    return ppa.prefill_attention(
+        dev["q"], dev["k_new"], dev["v_new"], dev["k_cache"], dev["v_cache"],
+        dev["block_table"], dev["query_start_loc"], dev["ctx_lens"], w.num_heads,
+        w.num_kv_heads, w.head_size, w.page_size, w.window_left, w.window_right, w.causal,
+        mm, w.scale, out=out, max_q_len=w.max_q_len)
+
+
+def out_to_f32(out):
+    import torch
+    return bf16_bits_to_f32(out.view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+def oracle_rows(w, s, rows, heads=None, cache_only=False, mm_ranges="default"):
+    mm = w.mm_ranges if isinstance(mm_ranges, str) else mm_ranges
+    return oracle.reference_rows(
+        w.f32("q"), None if cache_only else w.f32("k_new"),
+        None if cache_only else w.f32("v_new"), w.f32("k_cache"), w.f32("v_cache"),
+        w.block_table, w.query_start_loc, w.ctx_lens, w.num_heads, w.num_kv_heads,
+        w.head_size, w.page_size, w.window_left, w.window_right, w.causal, mm, w.scale, s,
+        rows, heads=heads)
+
+
+def oracle_full(w, cache_only=False):
+    return oracle.reference_prefill(
+        w.f32("q"), None if cache_only else w.f32("k_new"),
+        None if cache_only else w.f32("v_new"), w.f32("k_cache"), w.f32("v_cache"),
+        w.block_table, w.query_start_loc, w.ctx_lens, w.num_heads, w.num_kv_heads,
+        w.head_size, w.page_size, w.window_left, w.window_right, w.causal, w.mm_ranges,
+        w.scale)
+
+
+def compare(gpu, ref, what=""):
+    """Assert |gpu - ref| <= ATOL + RTOL*|ref| elementwise; return (max_abs, max_rel)."""
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    assert np.isfinite(gpu).all(), "non-finite GPU output " + what
+    err = np.abs(gpu.astype(np.float64) - ref.astype(np.float64))
+    bound = ATOL + RTOL * np.abs(ref.astype(np.float64))
+    bad = err > bound
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError("%s: %d elements out of tolerance, max err %.4g, first %s" % (
+            what, int(bad.sum()), float(err.max()), idx.tolist()))
+    rel = err / np.maximum(np.abs(ref), 1e-6)
+    return float(err.max()), float(rel[np.abs(ref) > 0.05].max() if (np.abs(ref) > 0.05).any()
+                                   else 0.0)
+
+
+def sample_rows(n, block_q, rng, extra=8):
+    """Rows that span tiles and tails: first/last rows, tile edges, random ones."""
+    cand = {0, n - 1, n // 2}
+    for t in range(0, n, block_q):
+        cand.update({t, min(n - 1, t + block_q - 1)})
+    rows = sorted(r for r in cand if 0 <= r < n)
+    if len(rows) > 24:
+        rows = sorted(set(rng.choice(rows, 24, replace=False).tolist()) | {0, n - 1})
+    rnd = rng.integers(0, n, size=min(extra, n)).tolist()
+    return np.array(sorted(set(rows) | set(rnd)), dtype=np.int64)

@@ -1,0 +1,114 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad scalar arguments without touching a GPU."""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_kv_prefill_attention_amd as ppa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ppa.library_path()):
+        ppa.build()
+    return ppa.load_library()
+
+
+def declared_functions():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for fn in sorted(os.listdir(inc)):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(inc, fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return names
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert "prefill_attention" in names and "prefill_attention_tile_bounds" in names
+    out = subprocess.run(["nm", "-D", "--defined-only", ppa.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for nm in names:
+        assert nm in exported, nm
+        assert hasattr(lib, nm)
+
+
+GOOD = dict(q=1, k_new=2, v_new=3, k_cache=4, v_cache=5, block_table=6, query_start_loc=7,
+            ctx_lens=8, num_heads=8, num_kv_heads=2, head_size=128, page_size=544,
+            window_left=-1, window_right=-1, causal=1, mm_ranges=None, scale=0.088, out=9,
+            num_seqs=4, total_q_tokens=100, max_q_len=40, num_pages=10, max_pages_per_seq=8,
+            max_mm_ranges=0)
+
+
+@pytest.mark.parametrize("change,code", [
+    ({}, ppa.OK),
+    ({"num_heads": 6, "num_kv_heads": 4}, ppa.ERR_INVALID_ARG),
+    ({"num_kv_heads": 0}, ppa.ERR_INVALID_ARG),
+    ({"page_size": 0}, ppa.ERR_INVALID_ARG),
+    ({"window_left": -2}, ppa.ERR_INVALID_ARG),
+    ({"window_right": -5}, ppa.ERR_INVALID_ARG),
+    ({"causal": 2}, ppa.ERR_INVALID_ARG),
+    ({"scale": 0.0}, ppa.ERR_INVALID_ARG),
+    ({"scale": float("nan")}, ppa.ERR_INVALID_ARG),
+    ({"scale": float("inf")}, ppa.ERR_INVALID_ARG),
+    ({"max_mm_ranges": 3}, ppa.ERR_INVALID_ARG),          # ranges without a pointer
+    ({"max_mm_ranges": 3, "mm_ranges": 10}, ppa.OK),
+    ({"max_mm_ranges": -1}, ppa.ERR_INVALID_ARG),
+    ({"k_new": None}, ppa.ERR_INVALID_ARG),                # only one of k_new/v_new
+    ({"k_new": None, "v_new": None}, ppa.OK),             # cache-sourced mode
+    ({"q": None}, ppa.ERR_INVALID_ARG),
+    ({"out": None}, ppa.ERR_INVALID_ARG),
+    ({"block_table": None}, ppa.ERR_INVALID_ARG),
+    ({"head_size": 96}, ppa.ERR_UNSUPPORTED),
+    ({"head_size": 64}, ppa.OK),
+    ({"head_size": 256}, ppa.OK),
+    ({"page_size": 1 << 17}, ppa.ERR_UNSUPPORTED),
+    ({"max_pages_per_seq": 1 << 20}, ppa.ERR_INVALID_ARG),  # beyond 2^24 positions
+    ({"num_seqs": 0, "q": None}, ppa.OK),                 # empty batch: nothing to do
+    ({"max_q_len": 0}, ppa.OK),
+    ({"num_seqs": -1}, ppa.ERR_INVALID_ARG),
+])
+def test_validate_codes(lib, change, code):
+    args = dict(GOOD)
+    args.update(change)
+    assert ppa.validate(**args) == code
+
+
+def test_invalid_call_returns_before_launch(lib):
+    # an unsupported head size is rejected on the host, before any HIP call
+    import ctypes
+    rc = lib.prefill_attention(*([None] * 8), 8, 2, 96, 16, -1, -1, 1, None, 0.1, None,
+                               1, 10, 10, 1, 1, 0, None)
+    assert rc == ppa.ERR_UNSUPPORTED
+    rc = lib.prefill_attention(*([None] * 8), 8, 3, 128, 16, -1, -1, 1, None, 0.1, None,
+                               1, 10, 10, 1, 1, 0, None)
+    assert rc == ppa.ERR_INVALID_ARG
+
+
+def test_tile_config(lib):
+    assert ppa.tile_config(128, 64, 64) == (128, 64)
+    assert ppa.tile_config(64, 8, 8) == (128, 128)
+    assert ppa.tile_config(256, 8, 2) == (32, 32)     # 4 query heads share a tile
+    assert ppa.tile_config(256, 16, 8) == (64, 32)
+    assert ppa.tile_config(128, 64, 1) == (2, 64)     # MQA: 64 heads x 2 tokens
+    assert ppa.tile_config(128, 24, 8) == (128, 64)   # group 3 does not divide 128 rows
+    with pytest.raises(ppa.PrefillError):
+        ppa.tile_config(80, 8, 8)
+    with pytest.raises(ppa.PrefillError):
+        ppa.tile_config(128, 8, 3)
+
+
+def test_strerror(lib):
+    assert ppa.strerror(0) == "ok"
+    assert "invalid" in ppa.strerror(-1)
+    assert "unsupported" in ppa.strerror(-2)
+    assert "unknown" in ppa.strerror(7)

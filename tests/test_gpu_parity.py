@@ -1,0 +1,210 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bar: |gpu - oracle| <= 2e-2 + 2e-2 * |oracle| elementwise for bf16 outputs;
+tile bounds bit-exact.  The full-size configurations run in the same launch
+configuration as the benchmark and are compared on sampled rows (every head of
+each sampled row) that span tile edges and ragged tails; the small cases are
+compared on every output element.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.harness import (compare, oracle_full, oracle_rows, out_to_f32, run_gpu,
+                           sample_rows, to_device)
+from workloads import make_config, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    import torch
+    import paged_kv_prefill_attention_amd as ppa
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    ppa.load_library()
+
+
+def tile_q(w):
+    import paged_kv_prefill_attention_amd as ppa
+    return ppa.tile_config(w.head_size, w.num_heads, w.num_kv_heads)
+
+
+def check_sampled(w, out, seed, cache_only=False, mm_ranges="default", rows_per_seq=None):
+    bq, _ = tile_q(w)
+    rng = np.random.default_rng(seed)
+    worst = (0.0, 0.0)
+    for s in range(w.num_seqs):
+        n = int(w.q_lens[s])
+        if n == 0:
+            continue
+        rows = sample_rows(n, bq, rng)
+        q0 = int(w.query_start_loc[s])
+        ref = oracle_rows(w, s, rows, cache_only=cache_only, mm_ranges=mm_ranges)
+        e = compare(out[q0 + rows], ref, "%s seq %d" % (w.name, s))
+        worst = (max(worst[0], e[0]), max(worst[1], e[1]))
+    return worst
+
+
+def test_config1_tiny_full():
+    w = make_config(1)
+    out = out_to_f32(run_gpu(w))
+    compare(out, oracle_full(w), w.name)
+
+
+@pytest.mark.parametrize("cid,P", [(2, None), (3, 1040), (3, 1056), (4, None), (5, None)],
+                         ids=["c2_page544", "c3_page1040", "c3_page1056", "c4_window",
+                              "c5_mm_prefix"])
+def test_full_size_configs_sampled(cid, P):
+    w = make_config(cid, page_size=P)
+    out = out_to_f32(run_gpu(w))
+    assert np.isfinite(out).all()
+    err = check_sampled(w, out, seed=cid)
+    print("%s max_abs=%.3g max_rel=%.3g" % (w.name, err[0], err[1]), flush=True)
+
+
+def test_config3_page_sizes_bitwise_equal():
+    """Tiles never depend on pages: 1040 and 1056 give the same bits."""
+    import torch
+    a = run_gpu(make_config(3, page_size=1040))
+    b = run_gpu(make_config(3, page_size=1056))
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_config5_negative_control_mm_ranges_matter():
+    w = make_config(5)
+    with_mm = out_to_f32(run_gpu(w))
+    without = out_to_f32(run_gpu(w, mm_ranges=None))
+    rows = np.arange(0, int(w.q_lens[0]), 97)
+    assert np.abs(with_mm[rows] - without[rows]).max() > 0.05
+    ref = oracle_rows(w, 0, rows, mm_ranges=None)
+    compare(without[rows], ref, "config5 without ranges")
+
+
+def test_deterministic_bitwise():
+    import torch
+    w = make_config(2)
+    dev = to_device(w)
+    a = run_gpu(w, dev=dev).clone()
+    b = run_gpu(w, dev=dev)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+FUZZ_PAGES = [1, 7, 16, 128, 512, 544, 1040, 1056, 2048]
+FUZZ_HEADS = [(4, 4), (8, 2), (8, 1), (6, 2), (16, 16), (12, 4), (64, 1), (3, 3)]
+
+
+def fuzz_workload(rng, i, cache_only=False):
+    S = int(rng.integers(1, 5))
+    H, Hkv = FUZZ_HEADS[int(rng.integers(0, len(FUZZ_HEADS)))]
+    d = int(rng.choice([64, 128, 256]))
+    P = int(rng.choice(FUZZ_PAGES))
+    ctx = rng.integers(0, 700, size=S)
+    if rng.random() < 0.3:
+        ctx[int(rng.integers(0, S))] = 0
+    new = rng.integers(1, 300, size=S)
+    causal = bool(rng.integers(0, 2))
+    wl = int(rng.choice([-1, -1, 0, 5, 63, 64, 200]))
+    wr = int(rng.choice([-1, 0, 17, 64, 300]))
+    mm = None
+    if rng.random() < 0.4:
+        R = int(rng.integers(1, 5))
+        mm = np.zeros((S, R, 2), dtype=np.int32)
+        for s in range(S):
+            L = int(ctx[s] + new[s])
+            for r in range(R):
+                st = int(rng.integers(0, L + 10))
+                mm[s, r] = (st, st + int(rng.choice([0, 3, 40, 150, 400])))
+    return make_workload(seed=9000 + i, ctx_lens=ctx, q_lens=new, num_heads=H,
+                         num_kv_heads=Hkv, head_size=d, page_size=P, causal=causal,
+                         window_left=wl, window_right=wr, mm_ranges=mm,
+                         new_in_cache=cache_only, name="fuzz%d" % i)
+
+
+@pytest.mark.parametrize("chunk", range(6))
+def test_fuzz_full_outputs(chunk):
+    """60 random ragged batches: page sizes, head sizes, MHA/GQA/MQA, windows, ranges."""
+    rng = np.random.default_rng(31337 + chunk)
+    for i in range(10):
+        w = fuzz_workload(rng, chunk * 10 + i)
+        print("fuzz case", chunk * 10 + i, w.head_size, w.num_heads, w.num_kv_heads,
+              w.page_size, w.causal, w.window_left, w.window_right,
+              w.max_mm_ranges, flush=True)
+        out = out_to_f32(run_gpu(w))
+        compare(out, oracle_full(w), w.name)
+
+
+@pytest.mark.parametrize("chunk", range(2))
+def test_cache_sourced_mode(chunk):
+    """k_new = v_new = NULL: every position comes through the block table; the bits
+    equal those of the split mode on the same logical K/V."""
+    import torch
+    rng = np.random.default_rng(777 + chunk)
+    for i in range(6):
+        w = fuzz_workload(rng, 100 + chunk * 6 + i, cache_only=True)
+        out = run_gpu(w, cache_only=True)
+        compare(out_to_f32(out), oracle_full(w, cache_only=True), w.name + " cache-only")
+        split = run_gpu(w)
+        assert torch.equal(out.view(torch.int16), split.view(torch.int16))
+
+
+def test_paging_invariance_bitwise():
+    import torch
+    outs = []
+    for P, ts in [(16, 1), (16, 2), (544, 3), (1056, 4), (7, 5), (1, 6)]:
+        w = make_workload(seed=4242, table_seed=ts, ctx_lens=[1500, 0, 613, 97],
+                          q_lens=[300, 129, 64, 1], num_heads=8, num_kv_heads=2,
+                          head_size=128, page_size=P, causal=True)
+        outs.append(run_gpu(w).view(torch.int16).clone())
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+def test_edge_cases():
+    import torch
+    # empty sequences between non-empty ones, a single-token sequence, context
+    # that ends mid-page, page size 1
+    for P in (1, 5, 16):
+        w = make_workload(seed=17, ctx_lens=[33, 50, 0, 7, 0], q_lens=[0, 1, 130, 0, 2],
+                          num_heads=4, num_kv_heads=2, head_size=64, page_size=P, causal=True)
+        compare(out_to_f32(run_gpu(w)), oracle_full(w), "edge P=%d" % P)
+    # zero windows, right-only window, degenerate and out-of-sequence ranges
+    mm = np.array([[[5, 5], [40, 300], [2, 9]]], dtype=np.int32)
+    for causal, wl, wr in [(False, 0, 0), (False, -1, 0), (False, 0, -1), (True, 0, -1),
+                           (True, 3, -1), (False, 2, 1)]:
+        w = make_workload(seed=18, ctx_lens=[20], q_lens=[150], num_heads=2, num_kv_heads=1,
+                          head_size=128, page_size=16, causal=causal, window_left=wl,
+                          window_right=wr, mm_ranges=mm)
+        compare(out_to_f32(run_gpu(w)), oracle_full(w), "edge window %s" % ((causal, wl, wr),))
+    # empty batch: nothing launched, output untouched
+    import paged_kv_prefill_attention_amd as ppa
+    dev = "cuda"
+    q = torch.empty((0, 4, 64), dtype=torch.bfloat16, device=dev)
+    kc = torch.zeros((1, 16, 2, 64), dtype=torch.bfloat16, device=dev)
+    out = ppa.prefill_attention(q, q[:, :2], q[:, :2], kc, kc,
+                                torch.zeros((0, 1), dtype=torch.int32, device=dev),
+                                torch.zeros((1,), dtype=torch.int32, device=dev),
+                                torch.zeros((0,), dtype=torch.int32, device=dev),
+                                4, 2, 64, 16, -1, -1, True, None, 0.125, max_q_len=0)
+    assert out.shape == (0, 4, 64)
+
+
+def test_tile_bounds_bitexact():
+    import torch
+    import paged_kv_prefill_attention_amd as ppa
+    cases = [make_config(c) for c in (1, 2, 4, 5)] + [make_config(3, page_size=1040)]
+    rng = np.random.default_rng(55)
+    for i in range(40):
+        cases.append(fuzz_workload(rng, 500 + i))
+    for w in cases:
+        dev = to_device(w)
+        got = ppa.tile_bounds(dev["query_start_loc"], dev["ctx_lens"], w.num_heads,
+                              w.num_kv_heads, w.head_size, w.window_left, w.window_right,
+                              w.causal, dev["mm_ranges"], w.max_q_len)
+        torch.cuda.synchronize()
+        bq, bn = tile_q(w)
+        ref = oracle.tile_bounds_all(w.ctx_lens, w.q_lens, bq, bn, w.causal, w.window_left,
+                                     w.window_right, w.mm_ranges)
+        assert np.array_equal(got.cpu().numpy(), ref), w.name
