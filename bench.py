@@ -1,0 +1,280 @@
+"""Benchmark: paged-KV prefill attention on one MI355X.
+
+One step = one launch of the whole hot path (work decode, tile bounds, page
+resolution, K/V gather, QK^T, mask, online softmax, PV, epilogue) over the
+ragged batch "ragged_batch_page544": 8 sequences with U[0,4096] cached tokens
+in 544-token pages (randomly permuted block tables) and U[1,1024] new tokens,
+64 query / 64 KV heads, head size 128, causal, bf16 inputs ~ N(0,1).
+
+Prints ONE JSON line.  ``value`` is useful TFLOP/s: 4 * head_size FLOP per
+allowed (query, key) pair per query head, divided by the mean time per step
+(HIP events on the launch stream, inputs resident in HBM).  ``roofline`` prices
+the same kernel time against the bf16 dense MFMA peak; ``cpu_baseline`` times
+the CPU oracle on a bounded sample of the same workload.
+
+``--suite FILE`` additionally times every configuration and the sliding-window
+length sweep and writes them to FILE (one JSON object per line).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "prefill attention useful TFLOP/s + ms/batch; % of MI355X bf16 MFMA peak"
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_prefill_attention_amd", "csrc",
+                          "prefill_attention.hip")
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(w) -> int:
+    """Q read + O write once per query row and head; K and V read once per key
+    position and KV head (cached + new)."""
+    d = w.head_size
+    qo = 2 * 2 * d * w.num_heads * w.total_q_tokens
+    kv = 2 * 2 * d * w.num_kv_heads * int(w.seq_lens().sum())
+    return qo + kv
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if the committed
+    summary was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_attention_%s.md" % workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_val or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_val.group(1))
+
+
+def time_launches(fn, steps: int, warmup: int):
+    """Run ``fn`` warmup times, then time ``steps`` launches with events on the
+    current stream.  Returns (mean ms per launch, per-launch ms list, wall s)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    span = starts[0].elapsed_time(ends[-1])
+    return span / steps, per, wall
+
+
+def to_device(w, cache_only=False):
+    """Upload a seeded workload (bf16 bit patterns, int32 metadata) to cuda:0."""
+    import numpy as np
+    import torch
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(
+            torch.bfloat16)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+    return dict(q=bf(w.q), k_new=None if cache_only else bf(w.k_new),
+                v_new=None if cache_only else bf(w.v_new), k_cache=bf(w.k_cache),
+                v_cache=bf(w.v_cache), block_table=i32(w.block_table),
+                query_start_loc=i32(w.query_start_loc), ctx_lens=i32(w.ctx_lens),
+                mm_ranges=None if w.mm_ranges is None else i32(w.mm_ranges))
+
+
+def make_launcher(w, cache_only=False):
+    import torch
+    import paged_kv_prefill_attention_amd as ppa
+    dev = to_device(w, cache_only=cache_only)
+    out = torch.empty_like(dev["q"])
+
+    def fn():
+        ppa.prefill_attention(dev["q"], dev["k_new"], dev["v_new"], dev["k_cache"],
+                              dev["v_cache"], dev["block_table"], dev["query_start_loc"],
+                              dev["ctx_lens"], w.num_heads, w.num_kv_heads, w.head_size,
+                              w.page_size, w.window_left, w.window_right, w.causal,
+                              dev["mm_ranges"], w.scale, out=out, max_q_len=w.max_q_len)
+    return fn, dev, out
+
+
+def count_useful_pairs(w) -> int:
+    """Allowed (query row, key) pairs for one query head.  Each query's allowed
+    keys form one interval holding its own position: the base window
+    [a - window_left, a | a + window_right | L-1], widened by every valid
+    multimodal range [st, en] (st < en) that holds the query, whose left edge
+    is clamped to the window; then clamped to [0, L-1]."""
+    import numpy as np
+    total = 0
+    for s in range(w.num_seqs):
+        c, n = int(w.ctx_lens[s]), int(w.q_lens[s])
+        L = c + n
+        a = c + np.arange(n, dtype=np.int64)
+        lo = a - w.window_left if w.window_left >= 0 else np.zeros_like(a)
+        if w.causal:
+            hi = a.copy()
+        elif w.window_right >= 0:
+            hi = a + w.window_right
+        else:
+            hi = np.full_like(a, L - 1)
+        for st, en in w.mm_list(s):
+            if st < en:
+                hold = (a >= st) & (a <= en)
+                left = np.maximum(st, a - w.window_left) if w.window_left >= 0 else st
+                lo = np.where(hold, np.minimum(lo, left), lo)
+                hi = np.where(hold, np.maximum(hi, en), hi)
+        lo, hi = np.maximum(lo, 0), np.minimum(hi, L - 1)
+        total += int(np.maximum(hi - lo + 1, 0).sum())
+    return total
+
+
+def useful_flop(w) -> int:
+    """4 * head_size FLOP (QK^T and PV) per allowed pair per query head."""
+    return 4 * w.head_size * w.num_heads * count_useful_pairs(w)
+
+
+def cpu_baseline(w, heads: int):
+    """Time the CPU oracle (as it stands) on heads [0, heads) of every sequence."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = 1
+    args = (w.f32("q"), w.f32("k_new"), w.f32("v_new"), w.f32("k_cache"), w.f32("v_cache"),
+            w.block_table, w.query_start_loc, w.ctx_lens, w.num_heads, w.num_kv_heads,
+            w.head_size, w.page_size, w.window_left, w.window_right, w.causal, w.mm_ranges,
+            w.scale)
+    t0 = time.perf_counter()
+    for s in range(w.num_seqs):
+        n = int(w.q_lens[s])
+        if n:
+            oracle.reference_rows(*args, s, np.arange(n), heads=range(heads))
+    el = time.perf_counter() - t0
+    flop = useful_flop(w) * heads // w.num_heads
+    return {"value": flop / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": "fp32 numpy oracle, query heads 0..%d of all %d sequences (all rows), "
+                      "%.1f s, %.3g useful FLOP; host %s, os.cpu_count()=%s, affinity=%d" % (
+                          heads - 1, w.num_seqs, el, flop, platform.processor() or "cpu",
+                          os.cpu_count(), len(os.sched_getaffinity(0)))}
+
+
+def run_suite(path, steps, warmup):
+    """Every configuration plus the sliding-window length sweep."""
+    import torch
+    from workloads import make_config
+    rows = []
+    cases = [(1, None, None), (2, None, None), (3, 1040, None), (3, 1056, None),
+             (4, None, None), (5, None, None)]
+    cases += [(4, None, n) for n in (2048, 4096, 8192, 16384, 32768, 65536)]
+    for cid, P, n in cases:
+        w = make_config(cid, page_size=P, new_tokens=n)
+        fn, dev, out = make_launcher(w)
+        ms, per, _ = time_launches(fn, steps, warmup)
+        per.sort()
+        flop = useful_flop(w)
+        rec = {"config": cid, "workload": w.name, "new_tokens": int(w.q_lens.sum()),
+               "ms_mean": ms, "ms_median": per[len(per) // 2],
+               "useful_tflops": flop / (ms / 1e3) / 1e12,
+               "frac_mfma_peak": flop / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+               "alg_gbs": algorithmic_bytes(w) / (ms / 1e3) / 1e9, "useful_flop": flop}
+        rows.append(rec)
+        print(json.dumps(rec), file=sys.stderr, flush=True)
+        del dev, out, fn
+        torch.cuda.empty_cache()
+    with open(path, "w") as f:
+        for r in rows:
+            f.write(json.dumps(r) + "\n")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-heads", type=int, default=16,
+                    help="query heads in the bounded CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--suite", default=None, help="also time every config; write JSON lines")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_prefill_attention_amd as ppa
+    from workloads import make_config
+
+    if not os.path.exists(ppa.library_path()):
+        ppa.build()
+    ppa.load_library()
+    torch.cuda.set_device(0)
+
+    w = make_config(2)
+    fn, dev, out = make_launcher(w)
+    flop = useful_flop(w)
+    torch.cuda.synchronize()
+    ms, per, wall = time_launches(fn, args.steps, args.warmup)
+    kernel_ms = sum(per) / len(per)
+    value = flop / (ms / 1e3) / 1e12
+    achieved = flop / (kernel_ms / 1e3) / 1e12
+    traffic = traffic_from_profiles(w.name)
+    bq, bn = ppa.tile_config(w.head_size, w.num_heads, w.num_kv_heads)
+    rec = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_size": w.head_size,
+                   "page_size": w.page_size, "causal": w.causal,
+                   "ctx_lens": w.ctx_lens.tolist(), "q_lens": w.q_lens.tolist(),
+                   "total_q_tokens": w.total_q_tokens, "useful_flop": flop,
+                   "block_q": bq, "block_n": bn, "seed": w.seed},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "alg_hbm_gbs": round(algorithmic_bytes(w) / (kernel_ms / 1e3) / 1e9, 1),
+        "wall_s_timed": round(wall, 4),
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    del dev, out, fn
+    torch.cuda.empty_cache()
+    if args.suite:
+        run_suite(args.suite, args.steps, args.warmup)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, min(args.cpu_heads, w.num_heads))
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
