@@ -1,28 +1,32 @@
 // Paged-KV prefill attention for MI355X (gfx950, CDNA4).
 //
-// One workgroup (4 wavefronts, 256 lanes) owns one Q tile: `block_q` query
-// tokens of one sequence times the `heads_per_tile` query heads of one GQA
-// group that it packs into 128 MFMA rows, so one K/V gather serves every head
-// of the group.  The workgroup walks the KV tiles [lo, hi) given by the tile
-// bound calculator (the window unioned with every multimodal range that
+// One workgroup owns one Q tile: `block_q` query tokens of one sequence times
+// the `heads_per_tile` query heads of one GQA group, packed into 32 MFMA rows
+// per wavefront (256 rows for 8 wavefronts), so one K/V gather serves every
+// head of the group.  The workgroup walks the KV tiles [lo, hi) given by the
+// tile bound calculator (the window unioned with every multimodal range that
 // overlaps the tile's queries; vLLM PR #50776 report, "Key source snippets";
 // vLLM PR #53147 report, "Implementation breakdown" item 2).  Per KV tile:
 //
 //   1. page-offset resolver: key position j < ctx_len is slot j % P of page
 //      block_table[j / P] (division by an invariant integer with a
-//      Granlund-Montgomery multiply-shift, PLDI 1994), j >= ctx_len is a row of
-//      the chunk's new K/V; tiles never depend on pages, so any page size works
-//      (vLLM PR #54194 report, "Features and motivation");
-//   2. coalesced 16-byte gather of K and V rows into LDS (K row-major, V
-//      transposed so the PV contraction reads keys contiguously);
-//   3. S^T = K Q^T on v_mfma_f32_32x32x16_bf16: every lane ends up holding
-//      one query row's scores, so softmax row reductions are in-lane plus one
-//      exchange with the lane 32 away;
+//      Granlund-Montgomery multiply-shift, PLDI 1994; block-table entries are
+//      fetched on the scalar unit), j >= ctx_len is a row of the chunk's new
+//      K/V, j >= L reads a zero row; tiles never depend on pages, so any page
+//      size works (vLLM PR #54194 report, "Features and motivation");
+//   2. coalesced gather: 16-byte global->LDS DMA (global_load_lds_dwordx4)
+//      into a ring of NSTAGE tile buffers, so NSTAGE-1 tiles are in flight
+//      while one is consumed; one barrier per tile.  K and V rows are stored
+//      row-major with XOR-swizzled 16-byte chunks (conflict-free reads);
+//   3. S^T = K Q^T on v_mfma_f32_32x32x16_bf16: every lane holds one query
+//      row's scores, so softmax row reductions are in-lane plus one
+//      v_permlane32_swap with the lane 32 away;
 //   4. the element mask, only on tiles that are not provably all-allowed;
 //   5. online softmax in the exp2 domain (Milakov & Gimelshein 2018, with the
 //      scale folded into exp2 as in FlashAttention-2, Dao 2023);
-//   6. O^T += V^T P^T on the same MFMA, P rounded to bf16 (round-to-nearest-
-//      even, v_cvt_pk_bf16_f32).
+//   6. O^T += V^T P^T on the same MFMA: P rounded to bf16 (round-to-nearest-
+//      even, v_cvt_pk_bf16_f32); the V^T operand comes straight from the
+//      row-major V tile through ds_read_b64_tr_b16.
 // The epilogue divides by the row sum and stores bf16.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -38,12 +42,17 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kRows = 32 * kWaves;  // MFMA rows (query token x head pairs) per workgroup
 constexpr int kMaxTokens = 1 << 24; // positions per sequence the resolver handles exactly
 constexpr int kMaxMmRanges = 4096;
+constexpr int kStageBytes = 32768;  // one K tile + one V tile: block_n * head_size * 2 B * 2
+
+// Rows past the end of a sequence are gathered from here: exact zeros.
+__device__ __attribute__((aligned(16))) uint16_t g_zero_row[256];
 
 struct KernelArgs {
   const uint16_t* q;
@@ -61,7 +70,7 @@ struct KernelArgs {
   int32_t group;           // query heads per KV head
   int32_t heads_per_tile;  // query heads of one group packed into a workgroup
   int32_t head_blocks;     // group / heads_per_tile
-  int32_t block_q;         // query tokens per Q tile = kRows / heads_per_tile
+  int32_t block_q;         // query tokens per Q tile = rows / heads_per_tile
   int32_t page_size;
   uint32_t page_magic;     // ceil(2^(24+l) / page_size), l = ceil(log2(page_size))
   int32_t page_shift;      // 24 + l
@@ -138,52 +147,86 @@ __device__ __forceinline__ int wave_min(int v) {
   return v;
 }
 
-__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) {
-  return (a & 0xffffu) | (b << 16);
+// max over the lane pair (l, l ^ 32): v_permlane32_swap exchanges the two
+// halves of the wave, so both lanes of a pair see both values.
+__device__ __forceinline__ float pair_max(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
 }
-__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
+__device__ __forceinline__ float pair_sum(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
-// Element offset of key position j (KV head g) in the cache or the new rows;
-// -1 when j is past the sequence (the row is zero-filled, never read).
-__device__ __forceinline__ int64_t key_offset(const KernelArgs& p, int s, int g, int j, int c,
-                                              int L, int q0, int D, bool& from_cache) {
-  from_cache = false;
-  if (j >= L) return -1;
-  const int cache_end = p.cache_only ? L : c;
-  if (j < cache_end) {
-    from_cache = true;
-    const uint32_t pg = (uint32_t)(((uint64_t)(uint32_t)j * p.page_magic) >> p.page_shift);
-    const int slot = j - (int)pg * p.page_size;
-    const int page = p.block_table[(int64_t)s * p.max_pages_per_seq + pg];
-    return (((int64_t)page * p.page_size + slot) * p.num_kv_heads + g) * D;
+// 16-byte asynchronous global->LDS copy: lane i writes lds_base + 16 i.  The
+// compiler does not track these copies; completion is awaited explicitly with
+// vm_wait<>() before the barrier that publishes a stage.
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gaddr), "s"(lds_base) : "memory", "m0");
+}
+// Block-table entry read on the scalar unit (s_load, counted by lgkmcnt), so a
+// lookup never waits on the vector-memory counter that tracks the copies in
+// flight.  `ptr` must be wave-uniform.
+__device__ __forceinline__ int scalar_load_i32(const int32_t* ptr) {
+  const uint64_t a = (uint64_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint64_t ua = ((uint64_t)hi << 32) | lo;
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ua) : "memory");
+  return v;
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// LDS tile layout: rows of D bf16 (one key each), 16-byte chunks XOR-swizzled
+// per row so that the MFMA operand reads hit distinct banks.
+template <int D>
+struct TileLayout {
+  static constexpr int CHUNKS = D / 8;
+  static constexpr int ROWS_PER_DMA = 512 / D;  // key rows per 1-KB DMA instruction
+  // K: 16 lanes read the same chunk of 16 consecutive rows.
+  __device__ static __forceinline__ int kslot(int row, int chunk) {
+    return D == 64 ? (chunk ^ ((row >> 1) & 7)) : (chunk ^ (row & 15));
   }
-  return ((int64_t)(q0 + j - c) * p.num_kv_heads + g) * D;
-}
+  // V: a 16-lane group reads 4 consecutive rows x 4 chunks (transpose read).
+  __device__ static __forceinline__ int vslot(int row, int chunk) {
+    return D == 64 ? (chunk ^ (((row >> 1) & 1) << 2)) : (chunk ^ ((row & 3) << 2));
+  }
+};
 
-template <int D, int BN>
-struct Tile {
-  static constexpr int KLD = D + 8;    // K row stride in LDS (elements): 16 B pad
-  static constexpr int VLD = BN + 4;   // V^T row stride in LDS (elements): 8 B pad
-  static constexpr int CHUNKS = D / 8; // 16-byte chunks per key row
-  static constexpr int QUADS = (BN / 4) * CHUNKS;  // (4 keys x 8 dims) loader units
-  static constexpr int QPT = QUADS / kThreads;     // units per lane
-  static_assert(QUADS % kThreads == 0, "tile must split evenly over the workgroup");
+template <int D, int NW>
+struct Config {
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int ROWS = 32 * NW;
+  static constexpr int BN = kStageBytes / (4 * D);          // keys per KV tile
+  static constexpr int DMA_PER_TENSOR = BN * D * 2 / 1024;  // 1-KB copies per tile per tensor
+  static constexpr int DMA_PER_WAVE = DMA_PER_TENSOR / NW;
+  static_assert(DMA_PER_TENSOR % NW == 0, "copies must split evenly over the wavefronts");
   static_assert(BN % 32 == 0 && D % 32 == 0, "MFMA blocking");
 };
 
-template <int D, int BN, int WAVES_PER_EU>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+template <int D, int NW, int NSTAGE, int WAVES_PER_EU>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
                           amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
 void prefill_attention_kernel(const KernelArgs p) {
-  using T = Tile<D, BN>;
+  using C = Config<D, NW>;
+  using Lay = TileLayout<D>;
+  constexpr int BN = C::BN;
   constexpr int KSTEPS = D / 16;   // QK^T contraction steps of 16 dims
   constexpr int NKB = BN / 32;     // 32-key blocks per KV tile
   constexpr int PSTEPS = BN / 16;  // PV contraction steps of 16 keys
   constexpr int NDB = D / 32;      // 32-dim blocks of the output
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BN * T::KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[D * T::VLD];
+  constexpr int TILE_ELEMS = BN * D;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[NSTAGE][2][TILE_ELEMS];
 
   // ---- work decode: blockIdx -> (Q tile from the end, sequence, head block)
   const int HB = p.num_kv_heads * p.head_blocks;
@@ -199,16 +242,18 @@ void prefill_attention_kernel(const KernelArgs p) {
   const int t = ntiles - 1 - z;  // heaviest (last) tiles are dispatched first
   const int c = p.ctx_lens[s];
   const int L = c + n;
+  const int cache_end = p.cache_only ? L : c;
   const int g = hb_all / p.head_blocks;
   const int hblk = hb_all % p.head_blocks;
   const int R = p.max_mm_ranges;
   const int32_t* ranges = R > 0 ? p.mm_ranges + (int64_t)s * R * 2 : nullptr;
+  const int32_t* bt = p.block_table + (int64_t)s * p.max_pages_per_seq;
 
   const int2 tb = kv_tile_range(c, n, t, p.block_q, BN, p.causal, p.window_left,
                                 p.window_right, ranges, R);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int half = lane >> 5;
   const int col = lane & 31;
@@ -228,6 +273,71 @@ void prefill_attention_kernel(const KernelArgs p) {
   const int w_hi_max = wave_max(valid ? hi_a : INT_MIN);
   const bool wave_active = w_hi_max != INT_MIN;
 
+  // ---- gather: wave `wave` issues copies id = wave + q*NW of each tensor; a
+  // copy fills key rows [id*ROWS_PER_DMA, +ROWS_PER_DMA), lane -> (row, slot).
+  const uint32_t smem_base =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u16*)&smem[0][0][0]);
+  const int lane_row = lane / Lay::CHUNKS;
+  const int lane_slot = lane % Lay::CHUNKS;
+  const int64_t kv_row_stride = (int64_t)p.num_kv_heads * D;
+  auto issue_tile = [&](int tile, int stage) {
+    const int j0 = tile * BN;
+#pragma unroll
+    for (int qi = 0; qi < C::DMA_PER_WAVE; ++qi) {
+      const int id = wave + qi * NW;
+      const int rbase = id * Lay::ROWS_PER_DMA;
+      const int js = j0 + rbase;             // first key of this copy (wave-uniform)
+      const int r = rbase + lane_row;         // tile row of this lane
+      const int j = js + lane_row;
+      const uint16_t* kp = g_zero_row;
+      const uint16_t* vp = g_zero_row;
+      if (js < cache_end) {
+        // block-table entries of the pages this copy touches, on the scalar unit
+        const int jl = min(js + Lay::ROWS_PER_DMA, cache_end) - 1;
+        const uint32_t pg_first = (uint32_t)(((uint64_t)(uint32_t)js * p.page_magic) >> p.page_shift);
+        const uint32_t pg_last = (uint32_t)(((uint64_t)(uint32_t)jl * p.page_magic) >> p.page_shift);
+        const uint32_t pg_l = (uint32_t)(((uint64_t)(uint32_t)j * p.page_magic) >> p.page_shift);
+        int page_l = 0;
+        for (uint32_t pg = pg_first; pg <= pg_last; ++pg) {
+          const int page = scalar_load_i32(bt + pg);
+          page_l = pg_l == pg ? page : page_l;
+        }
+        if (j < cache_end) {
+          const int slot = j - (int)pg_l * p.page_size;
+          const int64_t off = ((int64_t)page_l * p.page_size + slot) * kv_row_stride + (int64_t)g * D;
+          kp = p.k_cache + off;
+          vp = p.v_cache + off;
+        }
+      }
+      if (j >= cache_end && j < L) {
+        const int64_t off = (int64_t)(q0 + j - c) * kv_row_stride + (int64_t)g * D;
+        kp = p.k_new + off;
+        vp = p.v_new + off;
+      }
+      const uint32_t kdst = smem_base + (uint32_t)((stage * 2 + 0) * TILE_ELEMS * 2 + id * 1024);
+      const uint32_t vdst = smem_base + (uint32_t)((stage * 2 + 1) * TILE_ELEMS * 2 + id * 1024);
+      dma16(kp + 8 * Lay::kslot(r, lane_slot), kdst);
+      dma16(vp + 8 * Lay::vslot(r, lane_slot), vdst);
+    }
+  };
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
+  float m_run = -INFINITY;  // running row max of scale*log2(e)*score
+  float l_run = 0.f;        // running row sum (this lane half's keys)
+
+  // per-lane pieces of the transpose read of V: 16-lane group G, lane j16
+  const int grp = lane >> 4;
+  const int j16 = lane & 15;
+  const int v_row_in = 4 * (grp >> 1) + (j16 >> 2);          // + 16 ks2 + 8 r
+  const int v_dim_in = 16 * (grp & 1) + 4 * (j16 & 3);        // + 32 db
+
+  const int ntile = tb.y - tb.x;
+#pragma unroll
+  for (int i = 0; i < NSTAGE - 1; ++i)
+    if (i < ntile) issue_tile(tb.x + i, i);
+
   // ---- Q fragments: B operand of S^T = K Q^T (lane: row `col`, dims 16ks + 8half..+8)
   bf16x8 qf[KSTEPS];
   {
@@ -238,79 +348,37 @@ void prefill_attention_kernel(const KernelArgs p) {
       qf[ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  // The Q loads must be complete before the tile loop, or the compiler places
+  // its wait for them inside the loop, where it would drain the copies in
+  // flight on every iteration.  (vmcnt(0), expcnt and lgkmcnt unconstrained.)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
-  f32x16 oacc[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
-  float m_run = -INFINITY;  // running row max of scale*log2(e)*score
-  float l_run = 0.f;        // running row sum (this lane half's keys)
 
-  // ---- loader: each lane moves T::QPT units of 4 consecutive keys x 8 dims
-  u32x4 kreg[T::QPT][4];
-  u32x4 vreg[T::QPT][4];
-  auto load_tile = [&](int tile) {
-    const int j0 = tile * BN;
-#pragma unroll
-    for (int u = 0; u < T::QPT; ++u) {
-      const int unit = tid + u * kThreads;
-      const int kq = unit / T::CHUNKS;
-      const int kc = unit - kq * T::CHUNKS;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bool from_cache;
-        const int64_t off = key_offset(p, s, g, j0 + 4 * kq + i, c, L, q0, D, from_cache);
-        if (off < 0) {
-          kreg[u][i] = u32x4{0, 0, 0, 0};
-          vreg[u][i] = u32x4{0, 0, 0, 0};
-        } else {
-          const uint16_t* kb = from_cache ? p.k_cache : p.k_new;
-          const uint16_t* vb = from_cache ? p.v_cache : p.v_new;
-          kreg[u][i] = *(const u32x4*)(kb + off + 8 * kc);
-          vreg[u][i] = *(const u32x4*)(vb + off + 8 * kc);
-        }
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int u = 0; u < T::QPT; ++u) {
-      const int unit = tid + u * kThreads;
-      const int kq = unit / T::CHUNKS;
-      const int kc = unit - kq * T::CHUNKS;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *(u32x4*)(k_lds + (4 * kq + i) * T::KLD + 8 * kc) = kreg[u][i];
-      // 4 keys x 8 dims -> 8 rows of V^T, 4 consecutive keys each
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const u32x2 even = {pack_lo16(vreg[u][0][e2], vreg[u][1][e2]),
-                            pack_lo16(vreg[u][2][e2], vreg[u][3][e2])};
-        const u32x2 odd = {pack_hi16(vreg[u][0][e2], vreg[u][1][e2]),
-                           pack_hi16(vreg[u][2][e2], vreg[u][3][e2])};
-        *(u32x2*)(v_lds + (8 * kc + 2 * e2) * T::VLD + 4 * kq) = even;
-        *(u32x2*)(v_lds + (8 * kc + 2 * e2 + 1) * T::VLD + 4 * kq) = odd;
-      }
-    }
-  };
+  for (int it = 0; it < ntile; ++it) {
+    // copies of this tile are done once at most `after` later tiles are in flight
+    const int after = min(NSTAGE - 2, ntile - 1 - it);
+    if (after >= 2) vm_wait<2 * 2 * C::DMA_PER_WAVE>();
+    else if (after == 1) vm_wait<2 * C::DMA_PER_WAVE>();
+    else vm_wait<0>();
+    block_barrier();
+    if (it + NSTAGE - 1 < ntile) issue_tile(tb.x + it + NSTAGE - 1, (it + NSTAGE - 1) % NSTAGE);
 
-  if (tb.x < tb.y) load_tile(tb.x);
-  for (int tile = tb.x; tile < tb.y; ++tile) {
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile();
-    __syncthreads();
-    if (tile + 1 < tb.y) load_tile(tile + 1);  // in flight during this tile's math
-    const int j0 = tile * BN;
+    const int stage = it % NSTAGE;
+    const int j0 = (tb.x + it) * BN;
     if (!wave_active || j0 > w_hi_max || j0 + BN - 1 < w_lo_min) continue;
     const bool interior = j0 >= w_lo_max && j0 + BN - 1 <= w_hi_min;
+    const lds_u16* ks_lds = (const lds_u16*)&smem[stage][0][0];
+    const lds_u16* vs_lds = (const lds_u16*)&smem[stage][1][0];
 
     // S^T[key][query] = K Q^T
     f32x16 sacc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       sacc[kb] = f32x16{};
+      const int krow = kb * 32 + col;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const u32x4 a = *(const u32x4*)(k_lds + (kb * 32 + col) * T::KLD + 16 * ks + 8 * half);
+        const u32x4 a = *(const lds_u32x4*)(ks_lds + krow * D + 8 * Lay::kslot(krow, 2 * ks + half));
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                           qf[ks], sacc[kb], 0, 0, 0);
       }
@@ -330,7 +398,7 @@ void prefill_attention_kernel(const KernelArgs p) {
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = pair_max(mx);
     const float m_new = fmaxf(m_run, mx * p.scale_log2);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
@@ -361,22 +429,29 @@ void prefill_attention_kernel(const KernelArgs p) {
                        sacc[ks2 >> 1][8 * (ks2 & 1) + 6], sacc[ks2 >> 1][8 * (ks2 & 1) + 7]};
       pf[ks2] = __builtin_convertvector(v, bf16x8);
     }
-    // O^T[dim][query] += V^T P^T; A element e holds key 16ks2 + 8(e/4) + 4half + e%4
+    // O^T[dim][query] += V^T P^T.  A element e holds key 16ks2 + 8(e/4) + 4half + e%4 at
+    // dim 32db + col: two transpose reads of 4 keys x 16 dims per 16-lane group.
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int ks2 = 0; ks2 < PSTEPS; ++ks2) {
-        const uint16_t* vp = v_lds + (db * 32 + col) * T::VLD + 16 * ks2 + 4 * half;
-        const u32x2 lo = *(const u32x2*)vp;
-        const u32x2 hi = *(const u32x2*)(vp + 8);
-        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+        const int dim = 32 * db + v_dim_in;
+        const int r0 = 16 * ks2 + v_row_in;
+        const int r1 = r0 + 8;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vs_lds + r0 * D + 8 * Lay::vslot(r0, dim >> 3) + (dim & 7)));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(vs_lds + r1 * D + 8 * Lay::vslot(r1, dim >> 3) + (dim & 7)));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+        const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                           pf[ks2], oacc[db], 0, 0, 0);
       }
   }
 
   // ---- epilogue: O / l -> bf16; lane holds dims 32db + 8(r/4) + 4half + r%4
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(l_run);
   if (valid) {
     const float inv = 1.f / l_tot;
     uint16_t* orow = p.out + ((int64_t)(q0 + tok) * p.num_heads + head) * D;
@@ -427,21 +502,21 @@ int gcd_int(int a, int b) {
   return a;
 }
 
+// Wavefronts per workgroup: 8 (two per SIMD) while the per-lane state fits 256
+// registers, 4 (one per SIMD, 512 registers) for head size 256.
+int waves_for(int head_size) { return head_size == 256 ? 4 : 8; }
+
 int choose_tiles(int head_size, int num_heads, int num_kv_heads, TileChoice* tc) {
   if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
     return PAGED_PREFILL_ERR_INVALID_ARG;
-  int bn;
-  switch (head_size) {
-    case 64: bn = 128; break;
-    case 128: bn = 64; break;
-    case 256: bn = 32; break;
-    default: return PAGED_PREFILL_ERR_UNSUPPORTED;
-  }
+  if (head_size != 64 && head_size != 128 && head_size != 256)
+    return PAGED_PREFILL_ERR_UNSUPPORTED;
+  const int rows = 32 * waves_for(head_size);
   const int group = num_heads / num_kv_heads;
-  const int hpt = gcd_int(group, kRows);  // heads of one group that share a tile
-  tc->block_n = bn;
+  const int hpt = gcd_int(group, rows);  // heads of one group that share a tile
+  tc->block_n = kStageBytes / (4 * head_size);
   tc->heads_per_tile = hpt;
-  tc->block_q = kRows / hpt;
+  tc->block_q = rows / hpt;
   return PAGED_PREFILL_OK;
 }
 
@@ -483,11 +558,11 @@ void page_magic(int page_size, uint32_t* magic, int* shift) {
   *shift = 24 + l;
 }
 
-template <int D, int BN, int W>
+template <int D, int NW, int NSTAGE, int W>
 hipError_t launch(const KernelArgs& a, uint32_t grid, hipStream_t stream) {
   void* args[] = {(void*)&a};
-  return hipLaunchKernel((const void*)&prefill_attention_kernel<D, BN, W>, dim3(grid),
-                         dim3(kThreads), args, 0, stream);
+  return hipLaunchKernel((const void*)&prefill_attention_kernel<D, NW, NSTAGE, W>, dim3(grid),
+                         dim3(64 * NW), args, 0, stream);
 }
 
 }  // namespace
@@ -583,9 +658,9 @@ int prefill_attention(const void* q, const void* k_new, const void* v_new,
   if (grid > 0x7fffffff) return PAGED_PREFILL_ERR_UNSUPPORTED;
   hipError_t err;
   switch (head_size) {
-    case 64: err = launch<64, 128, 2>(a, (uint32_t)grid, stream); break;
-    case 128: err = launch<128, 64, 2>(a, (uint32_t)grid, stream); break;
-    default: err = launch<256, 32, 1>(a, (uint32_t)grid, stream); break;
+    case 64: err = launch<64, 8, 4, 2>(a, (uint32_t)grid, stream); break;
+    case 128: err = launch<128, 8, 4, 2>(a, (uint32_t)grid, stream); break;
+    default: err = launch<256, 4, 4, 1>(a, (uint32_t)grid, stream); break;
   }
   return err == hipSuccess ? PAGED_PREFILL_OK : PAGED_PREFILL_ERR_HIP;
 }
