@@ -220,6 +220,9 @@ def main():
                     help="query heads in the bounded CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", default=None, help="also time every config; write JSON lines")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead: time a plain device copy of this many bytes (the "
+                         "reference kernel for scaling the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -234,6 +237,14 @@ def main():
         ppa.build()
     ppa.load_library()
     torch.cuda.set_device(0)
+
+    if args.copy_bytes:
+        src = torch.ones(args.copy_bytes // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        ms, _, _ = time_launches(lambda: dst.copy_(src), args.steps, args.warmup)
+        print(json.dumps({"copy_bytes": args.copy_bytes, "ms": ms,
+                          "gbs_read_plus_write": 2 * args.copy_bytes / (ms / 1e3) / 1e9}))
+        return
 
     w = make_config(2)
     fn, dev, out = make_launcher(w)

@@ -49,7 +49,19 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 constexpr int kMaxTokens = 1 << 24; // positions per sequence the resolver handles exactly
 constexpr int kMaxMmRanges = 4096;
-constexpr int kStageBytes = 32768;  // one K tile + one V tile: block_n * head_size * 2 B * 2
+
+// Tile shape per head size: wavefronts per workgroup (32 query rows each), keys
+// per KV tile, depth of the LDS ring, and wavefronts per SIMD.  Overridable at
+// build time (-DPREFILL_TILE_D128=4,32,4,2) for tile-shape sweeps.
+#ifndef PREFILL_TILE_D64
+#define PREFILL_TILE_D64 4, 64, 4, 2
+#endif
+#ifndef PREFILL_TILE_D128
+#define PREFILL_TILE_D128 8, 64, 4, 2
+#endif
+#ifndef PREFILL_TILE_D256
+#define PREFILL_TILE_D256 8, 32, 4, 2
+#endif
 
 // Rows past the end of a sequence are gathered from here: exact zeros.
 __device__ __attribute__((aligned(16))) uint16_t g_zero_row[256];
@@ -194,31 +206,65 @@ struct TileLayout {
   static constexpr int CHUNKS = D / 8;
   static constexpr int ROWS_PER_DMA = 512 / D;  // key rows per 1-KB DMA instruction
   // K: 16 lanes read the same chunk of 16 consecutive rows.
-  __device__ static __forceinline__ int kslot(int row, int chunk) {
-    return D == 64 ? (chunk ^ ((row >> 1) & 7)) : (chunk ^ (row & 15));
+  __device__ static __forceinline__ int kswz(int row) {
+    return D == 64 ? ((row >> 1) & 7) : (row & 15);
   }
+  __device__ static __forceinline__ int kslot(int row, int chunk) { return chunk ^ kswz(row); }
   // V: a 16-lane group reads 4 consecutive rows x 4 chunks (transpose read).
-  __device__ static __forceinline__ int vslot(int row, int chunk) {
-    return D == 64 ? (chunk ^ (((row >> 1) & 1) << 2)) : (chunk ^ ((row & 3) << 2));
+  __device__ static __forceinline__ int vswz(int row) {
+    return D == 64 ? ((((row >> 1) & 1)) << 2) : ((row & 3) << 2);
   }
+  __device__ static __forceinline__ int vslot(int row, int chunk) { return chunk ^ vswz(row); }
+  // The swizzle only touches address bits below the row stride (2D bytes), so
+  // the byte offset of chunk (2ks + half) in row r is
+  //   (r*2D + 16*(half ^ kswz(r))) ^ (32*ks)
+  // and the transpose-read offset of dim block db is (base) ^ (64*db): one
+  // lane-invariant base per operand, one XOR per read.
 };
 
-template <int D, int NW>
-struct Config {
+template <int D_, int NW_, int BN_, int NSTAGE_, int WPE_>
+struct TileShape {
+  static constexpr int D = D_;
+  static constexpr int NW = NW_;
+  static constexpr int BN = BN_;          // keys per KV tile
+  static constexpr int NSTAGE = NSTAGE_;  // LDS ring depth (NSTAGE - 1 tiles in flight)
+  static constexpr int WPE = WPE_;        // wavefronts per SIMD
   static constexpr int THREADS = 64 * NW;
   static constexpr int ROWS = 32 * NW;
-  static constexpr int BN = kStageBytes / (4 * D);          // keys per KV tile
   static constexpr int DMA_PER_TENSOR = BN * D * 2 / 1024;  // 1-KB copies per tile per tensor
   static constexpr int DMA_PER_WAVE = DMA_PER_TENSOR / NW;
+  static constexpr int LDS_BYTES = NSTAGE * 2 * BN * D * 2;
   static_assert(DMA_PER_TENSOR % NW == 0, "copies must split evenly over the wavefronts");
   static_assert(BN % 32 == 0 && D % 32 == 0, "MFMA blocking");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 6, "ring depth");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
+template <int D> struct ShapeFor;
+template <> struct ShapeFor<64> { using T = TileShape<64, PREFILL_TILE_D64>; };
+template <> struct ShapeFor<128> { using T = TileShape<128, PREFILL_TILE_D128>; };
+template <> struct ShapeFor<256> { using T = TileShape<256, PREFILL_TILE_D256>; };
 
-template <int D, int NW, int NSTAGE, int WAVES_PER_EU>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW),
-                          amdgpu_waves_per_eu(WAVES_PER_EU, WAVES_PER_EU)))
+// Wait until at most `after` later tiles' copies (PER_TILE each) are in flight.
+template <int PER_TILE, int MAX_AFTER>
+__device__ __forceinline__ void wait_copies(int after) {
+  if constexpr (MAX_AFTER > 0) {
+    if (after >= MAX_AFTER) {
+      vm_wait<PER_TILE * MAX_AFTER>();
+      return;
+    }
+    wait_copies<PER_TILE, MAX_AFTER - 1>(after);
+  } else {
+    vm_wait<0>();
+  }
+}
+
+template <typename C>
+__global__ __attribute__((amdgpu_flat_work_group_size(C::THREADS, C::THREADS),
+                          amdgpu_waves_per_eu(C::WPE, C::WPE)))
 void prefill_attention_kernel(const KernelArgs p) {
-  using C = Config<D, NW>;
+  constexpr int D = C::D;
+  constexpr int NW = C::NW;
+  constexpr int NSTAGE = C::NSTAGE;
   using Lay = TileLayout<D>;
   constexpr int BN = C::BN;
   constexpr int KSTEPS = D / 16;   // QK^T contraction steps of 16 dims
@@ -267,10 +313,11 @@ void prefill_attention_kernel(const KernelArgs p) {
   int lo_a = 1, hi_a = 0;
   if (valid)
     row_interval(c + tok, L, p.causal, p.window_left, p.window_right, ranges, R, lo_a, hi_a);
-  const int w_lo_max = wave_max(valid ? lo_a : INT_MIN);
-  const int w_hi_min = wave_min(valid ? hi_a : INT_MAX);
-  const int w_lo_min = wave_min(valid ? lo_a : INT_MAX);
-  const int w_hi_max = wave_max(valid ? hi_a : INT_MIN);
+  // wave-uniform summaries of the rows' key intervals (scalar registers)
+  const int w_lo_max = __builtin_amdgcn_readfirstlane(wave_max(valid ? lo_a : INT_MIN));
+  const int w_hi_min = __builtin_amdgcn_readfirstlane(wave_min(valid ? hi_a : INT_MAX));
+  const int w_lo_min = __builtin_amdgcn_readfirstlane(wave_min(valid ? lo_a : INT_MAX));
+  const int w_hi_max = __builtin_amdgcn_readfirstlane(wave_max(valid ? hi_a : INT_MIN));
   const bool wave_active = w_hi_max != INT_MIN;
 
   // ---- gather: wave `wave` issues copies id = wave + q*NW of each tensor; a
@@ -280,6 +327,7 @@ void prefill_attention_kernel(const KernelArgs p) {
   const int lane_row = lane / Lay::CHUNKS;
   const int lane_slot = lane % Lay::CHUNKS;
   const int64_t kv_row_stride = (int64_t)p.num_kv_heads * D;
+  const int64_t lane_row_off = (int64_t)lane_row * kv_row_stride;
   auto issue_tile = [&](int tile, int stage) {
     const int j0 = tile * BN;
 #pragma unroll
@@ -289,9 +337,26 @@ void prefill_attention_kernel(const KernelArgs p) {
       const int js = j0 + rbase;             // first key of this copy (wave-uniform)
       const int r = rbase + lane_row;         // tile row of this lane
       const int j = js + lane_row;
+      const int je = js + Lay::ROWS_PER_DMA;  // one past the copy's last key
       const uint16_t* kp = g_zero_row;
       const uint16_t* vp = g_zero_row;
-      if (js < cache_end) {
+      // Common cases, decided per wave: every key of the copy in one cache
+      // page, every key a new row, or every key past the sequence.  The row
+      // base is then computed on the scalar unit.
+      const uint32_t pg0 = (uint32_t)(((uint64_t)(uint32_t)js * p.page_magic) >> p.page_shift);
+      const int slot0 = js - (int)pg0 * p.page_size;
+      if (je <= cache_end && slot0 + Lay::ROWS_PER_DMA <= p.page_size) {
+        const int page = scalar_load_i32(bt + pg0);
+        const int64_t base = ((int64_t)page * p.page_size + slot0) * kv_row_stride + (int64_t)g * D;
+        kp = p.k_cache + base + lane_row_off;
+        vp = p.v_cache + base + lane_row_off;
+      } else if (js >= cache_end && je <= L) {
+        const int64_t base = (int64_t)(q0 + js - c) * kv_row_stride + (int64_t)g * D;
+        kp = p.k_new + base + lane_row_off;
+        vp = p.v_new + base + lane_row_off;
+      } else if (js >= L) {
+        // zero rows
+      } else if (js < cache_end) {
         // block-table entries of the pages this copy touches, on the scalar unit
         const int jl = min(js + Lay::ROWS_PER_DMA, cache_end) - 1;
         const uint32_t pg_first = (uint32_t)(((uint64_t)(uint32_t)js * p.page_magic) >> p.page_shift);
@@ -309,7 +374,8 @@ void prefill_attention_kernel(const KernelArgs p) {
           vp = p.v_cache + off;
         }
       }
-      if (j >= cache_end && j < L) {
+      if (js < L && !(je <= cache_end && slot0 + Lay::ROWS_PER_DMA <= p.page_size) &&
+          !(js >= cache_end && je <= L) && j >= cache_end && j < L) {
         const int64_t off = (int64_t)(q0 + j - c) * kv_row_stride + (int64_t)g * D;
         kp = p.k_new + off;
         vp = p.v_new + off;
@@ -324,14 +390,27 @@ void prefill_attention_kernel(const KernelArgs p) {
   f32x16 oacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
-  float m_run = -INFINITY;  // running row max of scale*log2(e)*score
+  // Reference max of scale*log2(e)*score used as the exp2 offset.  It only
+  // moves when a row's max grows by more than kLazy (factor 2^kLazy), so the
+  // O rescale is rare; the softmax is unchanged because numerator and
+  // denominator share the offset, and p <= 2^kLazy stays far from overflow.
+  // Starts finite so that fully masked entries give exp2(-inf) = 0.
+  constexpr float kLazy = 8.f;
+  float m_run = -1e30f;
   float l_run = 0.f;        // running row sum (this lane half's keys)
 
-  // per-lane pieces of the transpose read of V: 16-lane group G, lane j16
+  // Lane-invariant LDS byte offsets of the operand reads (stage 0).
+  // K (A operand of S^T): row `col` of each 32-key block, chunk 2ks + half.
+  const uint32_t k_lane = smem_base + (uint32_t)(col * 2 * D + 16 * (half ^ Lay::kswz(col)));
+  // V^T (A operand of O^T) via the transpose read: 16-lane group G reads rows
+  // 16ks2 + 8r + 4(G/2) + j16/4 and dims 32db + 16(G%2) + 4(j16%4).
   const int grp = lane >> 4;
   const int j16 = lane & 15;
-  const int v_row_in = 4 * (grp >> 1) + (j16 >> 2);          // + 16 ks2 + 8 r
-  const int v_dim_in = 16 * (grp & 1) + 4 * (j16 & 3);        // + 32 db
+  const int v_row_in = 4 * (grp >> 1) + (j16 >> 2);
+  const int v_dim_in = 16 * (grp & 1) + 4 * (j16 & 3);
+  const uint32_t v_lane = smem_base + (uint32_t)(v_row_in * 2 * D +
+                                                 16 * Lay::vslot(v_row_in, v_dim_in >> 3) +
+                                                 2 * (v_dim_in & 7));
 
   const int ntile = tb.y - tb.x;
 #pragma unroll
@@ -356,10 +435,7 @@ void prefill_attention_kernel(const KernelArgs p) {
 
   for (int it = 0; it < ntile; ++it) {
     // copies of this tile are done once at most `after` later tiles are in flight
-    const int after = min(NSTAGE - 2, ntile - 1 - it);
-    if (after >= 2) vm_wait<2 * 2 * C::DMA_PER_WAVE>();
-    else if (after == 1) vm_wait<2 * C::DMA_PER_WAVE>();
-    else vm_wait<0>();
+    wait_copies<2 * C::DMA_PER_WAVE, NSTAGE - 2>(ntile - 1 - it);
     block_barrier();
     if (it + NSTAGE - 1 < ntile) issue_tile(tb.x + it + NSTAGE - 1, (it + NSTAGE - 1) % NSTAGE);
 
@@ -367,18 +443,18 @@ void prefill_attention_kernel(const KernelArgs p) {
     const int j0 = (tb.x + it) * BN;
     if (!wave_active || j0 > w_hi_max || j0 + BN - 1 < w_lo_min) continue;
     const bool interior = j0 >= w_lo_max && j0 + BN - 1 <= w_hi_min;
-    const lds_u16* ks_lds = (const lds_u16*)&smem[stage][0][0];
-    const lds_u16* vs_lds = (const lds_u16*)&smem[stage][1][0];
 
     // S^T[key][query] = K Q^T
     f32x16 sacc[NKB];
+    uint32_t kbase = k_lane + (uint32_t)(stage * 2 * TILE_ELEMS * 2);
+    asm volatile("" : "+v"(kbase));  // keep the per-read XORs in the loop (no hoisting)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       sacc[kb] = f32x16{};
-      const int krow = kb * 32 + col;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const u32x4 a = *(const lds_u32x4*)(ks_lds + krow * D + 8 * Lay::kslot(krow, 2 * ks + half));
+        const uint32_t addr = (kbase + (uint32_t)(kb * 32 * D * 2)) ^ (uint32_t)(32 * ks);
+        const u32x4 a = *(const lds_u32x4*)(uintptr_t)addr;
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                           qf[ks], sacc[kb], 0, 0, 0);
       }
@@ -398,27 +474,28 @@ void prefill_attention_kernel(const KernelArgs p) {
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = pair_max(mx);
-    const float m_new = fmaxf(m_run, mx * p.scale_log2);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    mx = pair_max(mx) * p.scale_log2;
+    const bool grow = mx > m_run + kLazy;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform branch
+      const float m_new = grow ? mx : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      m_run = m_new;
+    }
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], p.scale_log2, -m_use));
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], p.scale_log2, -m_run));
         sacc[kb][r] = e;
         rs += e;
       }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
+    l_run += rs;
     // P^T as B operands: PV step ks2 covers keys 16ks2..16ks2+15
     bf16x8 pf[PSTEPS];
 #pragma unroll
@@ -431,17 +508,16 @@ void prefill_attention_kernel(const KernelArgs p) {
     }
     // O^T[dim][query] += V^T P^T.  A element e holds key 16ks2 + 8(e/4) + 4half + e%4 at
     // dim 32db + col: two transpose reads of 4 keys x 16 dims per 16-lane group.
+    uint32_t vbase = v_lane + (uint32_t)((stage * 2 + 1) * TILE_ELEMS * 2);
+    asm volatile("" : "+v"(vbase));
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int ks2 = 0; ks2 < PSTEPS; ++ks2) {
-        const int dim = 32 * db + v_dim_in;
-        const int r0 = 16 * ks2 + v_row_in;
-        const int r1 = r0 + 8;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vs_lds + r0 * D + 8 * Lay::vslot(r0, dim >> 3) + (dim & 7)));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(vs_lds + r1 * D + 8 * Lay::vslot(r1, dim >> 3) + (dim & 7)));
+        const uint32_t a0 = (vbase ^ (uint32_t)(64 * db)) + (uint32_t)(16 * ks2 * 2 * D);
+        const uint32_t a1 = a0 + (uint32_t)(8 * 2 * D);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a0);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a1);
         const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
         const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
         const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
@@ -504,17 +580,24 @@ int gcd_int(int a, int b) {
 
 // Wavefronts per workgroup: 8 (two per SIMD) while the per-lane state fits 256
 // registers, 4 (one per SIMD, 512 registers) for head size 256.
-int waves_for(int head_size) { return head_size == 256 ? 4 : 8; }
+template <int D> void shape_of(int* nw, int* bn) {
+  *nw = ShapeFor<D>::T::NW;
+  *bn = ShapeFor<D>::T::BN;
+}
 
 int choose_tiles(int head_size, int num_heads, int num_kv_heads, TileChoice* tc) {
   if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
     return PAGED_PREFILL_ERR_INVALID_ARG;
   if (head_size != 64 && head_size != 128 && head_size != 256)
     return PAGED_PREFILL_ERR_UNSUPPORTED;
-  const int rows = 32 * waves_for(head_size);
+  int nw, bn;
+  if (head_size == 64) shape_of<64>(&nw, &bn);
+  else if (head_size == 128) shape_of<128>(&nw, &bn);
+  else shape_of<256>(&nw, &bn);
+  const int rows = 32 * nw;
   const int group = num_heads / num_kv_heads;
   const int hpt = gcd_int(group, rows);  // heads of one group that share a tile
-  tc->block_n = kStageBytes / (4 * head_size);
+  tc->block_n = bn;
   tc->heads_per_tile = hpt;
   tc->block_q = rows / hpt;
   return PAGED_PREFILL_OK;
@@ -558,11 +641,12 @@ void page_magic(int page_size, uint32_t* magic, int* shift) {
   *shift = 24 + l;
 }
 
-template <int D, int NW, int NSTAGE, int W>
+template <int D>
 hipError_t launch(const KernelArgs& a, uint32_t grid, hipStream_t stream) {
+  using C = typename ShapeFor<D>::T;
   void* args[] = {(void*)&a};
-  return hipLaunchKernel((const void*)&prefill_attention_kernel<D, NW, NSTAGE, W>, dim3(grid),
-                         dim3(64 * NW), args, 0, stream);
+  return hipLaunchKernel((const void*)&prefill_attention_kernel<C>, dim3(grid),
+                         dim3(C::THREADS), args, 0, stream);
 }
 
 }  // namespace
@@ -658,9 +742,9 @@ int prefill_attention(const void* q, const void* k_new, const void* v_new,
   if (grid > 0x7fffffff) return PAGED_PREFILL_ERR_UNSUPPORTED;
   hipError_t err;
   switch (head_size) {
-    case 64: err = launch<64, 8, 4, 2>(a, (uint32_t)grid, stream); break;
-    case 128: err = launch<128, 8, 4, 2>(a, (uint32_t)grid, stream); break;
-    default: err = launch<256, 4, 4, 1>(a, (uint32_t)grid, stream); break;
+    case 64: err = launch<64>(a, (uint32_t)grid, stream); break;
+    case 128: err = launch<128>(a, (uint32_t)grid, stream); break;
+    default: err = launch<256>(a, (uint32_t)grid, stream); break;
   }
   return err == hipSuccess ? PAGED_PREFILL_OK : PAGED_PREFILL_ERR_HIP;
 }

@@ -95,11 +95,11 @@ def test_invalid_call_returns_before_launch(lib):
 
 
 def test_tile_config(lib):
-    # 8 wavefronts x 32 rows for head sizes 64/128, 4 x 32 rows for 256
+    # 8 wavefronts x 32 rows for head sizes 128/256, 4 x 32 rows for 64
     assert ppa.tile_config(128, 64, 64) == (256, 64)
-    assert ppa.tile_config(64, 8, 8) == (256, 128)
-    assert ppa.tile_config(256, 8, 2) == (32, 32)     # 4 query heads share a tile
-    assert ppa.tile_config(256, 16, 8) == (64, 32)
+    assert ppa.tile_config(64, 8, 8) == (128, 64)
+    assert ppa.tile_config(256, 8, 2) == (64, 32)     # 4 query heads share a tile
+    assert ppa.tile_config(256, 16, 8) == (128, 32)
     assert ppa.tile_config(128, 64, 1) == (4, 64)     # MQA: 64 heads x 4 tokens
     assert ppa.tile_config(128, 24, 8) == (256, 64)   # group 3 does not divide the rows
     with pytest.raises(ppa.PrefillError):
