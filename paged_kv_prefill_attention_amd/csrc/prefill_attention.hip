@@ -36,6 +36,7 @@
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
@@ -49,6 +50,8 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 constexpr int kMaxTokens = 1 << 24; // positions per sequence the resolver handles exactly
 constexpr int kMaxMmRanges = 4096;
+constexpr int kNumXcd = 8;         // MI355X: 8 accelerator complex dies, one L2 each
+constexpr int kSortMaxSeqs = 256;  // batches up to this size get heavy-first ordering
 
 // Tile shape per head size: wavefronts per workgroup (32 query rows each), keys
 // per KV tile, depth of the LDS ring, and wavefronts per SIMD.  Overridable at
@@ -94,6 +97,7 @@ struct KernelArgs {
   int32_t max_pages_per_seq;
   int32_t max_mm_ranges;
   int32_t cache_only;      // 1: every position comes from the cache
+  int32_t num_q_tiles;     // cdiv(max_q_len, block_q)
 };
 
 // ---------------------------------------------------------------------------
@@ -177,8 +181,20 @@ __device__ __forceinline__ float pair_sum(float x) {
 // vm_wait<>() before the barrier that publishes a stage.
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(gaddr), "s"(lds_base) : "memory", "m0");
+               :: "v"(gaddr), "s"(__builtin_amdgcn_readfirstlane(lds_base)) : "memory", "m0");
 }
+// Same copy from a wave-uniform base plus a 32-bit per-lane byte offset.
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+// Page index of position j: floor(j / page_size) by Granlund-Montgomery
+// multiply-shift (exact for j < 2^24).
+__device__ __forceinline__ int page_of(int j, uint32_t magic, int shift) {
+  return (int)(((uint64_t)(uint32_t)j * magic) >> shift);
+}
+
 // Block-table entry read on the scalar unit (s_load, counted by lgkmcnt), so a
 // lookup never waits on the vector-memory counter that tracks the copies in
 // flight.  `ptr` must be wave-uniform.
@@ -222,6 +238,87 @@ struct TileLayout {
   // lane-invariant base per operand, one XOR per read.
 };
 
+// ---------------------------------------------------------------------------
+// Work decode.  The dispatcher deals workgroup ids to the 8 XCDs round-robin
+// (id b runs on XCD b % 8 as its (b / 8)-th workgroup), and each XCD has its
+// own L2.  A work item is (sequence s, KV head g, Q tile t, head block); all
+// items of one (s, g) group read the same K/V stream, so they get consecutive
+// slots on one XCD and share its L2.  For up to kSortMaxSeqs sequences the
+// groups are ranked heavy-first (sequences by their key count L, then g) and
+// dealt to the XCDs round-robin by rank; within a group the last (heaviest)
+// Q tile comes first.  Larger batches deal g-major contiguous chunks.
+// ---------------------------------------------------------------------------
+struct WorkItem {
+  int s, g, hblk, t;
+  bool valid;
+};
+
+__device__ __forceinline__ int seq_ntiles(const int32_t* qsl, int s, int block_q) {
+  return (qsl[s + 1] - qsl[s] + block_q - 1) / block_q;
+}
+
+template <typename Args>
+__device__ WorkItem decode_work(const Args& p, int b, int tid, int nthreads, int* order,
+                                int* ntiles_by_rank) {
+  const int S = p.num_seqs;
+  const int Hkv = p.num_kv_heads;
+  const int HBLK = p.head_blocks;
+  const int x = b % kNumXcd;
+  int k = b / kNumXcd;
+  WorkItem w{0, 0, 0, 0, false};
+  if (S <= kSortMaxSeqs) {
+    for (int i = tid; i < S; i += nthreads) {
+      const int key_i = p.ctx_lens[i] + p.qsl[i + 1] - p.qsl[i];
+      int rank = 0;
+      for (int j = 0; j < S; ++j) {
+        const int key_j = p.ctx_lens[j] + p.qsl[j + 1] - p.qsl[j];
+        rank += (key_j > key_i) || (key_j == key_i && j < i);
+      }
+      order[rank] = i;
+      ntiles_by_rank[rank] = seq_ntiles(p.qsl, i, p.block_q);
+    }
+    __syncthreads();
+    // group rank r = sr * Hkv + g; XCD x owns ranks r = x (mod 8)
+    for (int sr = 0; sr < S; ++sr) {
+      const int g0 = ((x - sr * Hkv) % kNumXcd + kNumXcd) % kNumXcd;  // first g of this XCD
+      const int ng = g0 < Hkv ? (Hkv - 1 - g0) / kNumXcd + 1 : 0;
+      const int per_group = ntiles_by_rank[sr] * HBLK;
+      const int items = ng * per_group;
+      if (k < items) {
+        const int gi = k / per_group;
+        const int rem = k - gi * per_group;
+        const int z = rem / HBLK;
+        w.s = order[sr];
+        w.g = g0 + gi * kNumXcd;
+        w.hblk = rem - z * HBLK;
+        w.t = ntiles_by_rank[sr] - 1 - z;
+        w.valid = true;
+        return w;
+      }
+      k -= items;
+    }
+    return w;
+  }
+  // Large batches: XCD x owns a contiguous g-major range of (g, s) groups,
+  // each padded to the largest tile count (padding items exit).
+  const int groups = S * Hkv;
+  const int gper = (groups + kNumXcd - 1) / kNumXcd;
+  const int per_group = p.num_q_tiles * HBLK;
+  const int gidx = x * gper + k / per_group;
+  if (gidx >= groups || k >= gper * per_group) return w;
+  const int rem = k % per_group;
+  const int s = gidx % S;
+  const int nt = seq_ntiles(p.qsl, s, p.block_q);
+  const int z = rem / HBLK;
+  if (z >= nt) return w;
+  w.s = s;
+  w.g = gidx / S;
+  w.hblk = rem - z * HBLK;
+  w.t = nt - 1 - z;
+  w.valid = true;
+  return w;
+}
+
 template <int D_, int NW_, int BN_, int NSTAGE_, int WPE_>
 struct TileShape {
   static constexpr int D = D_;
@@ -234,9 +331,13 @@ struct TileShape {
   static constexpr int DMA_PER_TENSOR = BN * D * 2 / 1024;  // 1-KB copies per tile per tensor
   static constexpr int DMA_PER_WAVE = DMA_PER_TENSOR / NW;
   static constexpr int LDS_BYTES = NSTAGE * 2 * BN * D * 2;
+  // Block-table entries staged in LDS per workgroup (one workgroup per CU
+  // when the ring is large, two otherwise).
+  static constexpr int BT_CACHE = LDS_BYTES >= 96 * 1024 ? 4096 : 2048;
   static_assert(DMA_PER_TENSOR % NW == 0, "copies must split evenly over the wavefronts");
   static_assert(BN % 32 == 0 && D % 32 == 0, "MFMA blocking");
   static_assert(NSTAGE >= 2 && NSTAGE <= 6, "ring depth");
+
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 template <int D> struct ShapeFor;
@@ -270,27 +371,26 @@ void prefill_attention_kernel(const KernelArgs p) {
   constexpr int KSTEPS = D / 16;   // QK^T contraction steps of 16 dims
   constexpr int NKB = BN / 32;     // 32-key blocks per KV tile
   constexpr int PSTEPS = BN / 16;  // PV contraction steps of 16 keys
+  constexpr int QK_DEPTH = 4;      // K fragments in flight ahead of the QK MFMAs
+  constexpr int PV_DEPTH = 3;      // V fragments in flight ahead of the PV MFMAs
   constexpr int NDB = D / 32;      // 32-dim blocks of the output
   constexpr int TILE_ELEMS = BN * D;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[NSTAGE][2][TILE_ELEMS];
 
-  // ---- work decode: blockIdx -> (Q tile from the end, sequence, head block)
-  const int HB = p.num_kv_heads * p.head_blocks;
-  int b = blockIdx.x;
-  const int hb_all = b % HB;
-  b /= HB;
-  const int s = b % p.num_seqs;
-  const int z = b / p.num_seqs;
+  __shared__ int sched_seq[kSortMaxSeqs];
+  __shared__ int sched_ntiles[kSortMaxSeqs];
+  const int tid = threadIdx.x;
+  const WorkItem wi = decode_work(p, blockIdx.x, tid, C::THREADS, sched_seq, sched_ntiles);
+  if (!wi.valid) return;  // padding slot
+  const int s = wi.s;
+  const int g = wi.g;
+  const int hblk = wi.hblk;
+  const int t = wi.t;
   const int q0 = p.qsl[s];
   const int n = p.qsl[s + 1] - q0;
-  const int ntiles = (n + p.block_q - 1) / p.block_q;
-  if (z >= ntiles) return;  // padding tile of a shorter sequence
-  const int t = ntiles - 1 - z;  // heaviest (last) tiles are dispatched first
   const int c = p.ctx_lens[s];
   const int L = c + n;
   const int cache_end = p.cache_only ? L : c;
-  const int g = hb_all / p.head_blocks;
-  const int hblk = hb_all % p.head_blocks;
   const int R = p.max_mm_ranges;
   const int32_t* ranges = R > 0 ? p.mm_ranges + (int64_t)s * R * 2 : nullptr;
   const int32_t* bt = p.block_table + (int64_t)s * p.max_pages_per_seq;
@@ -298,7 +398,6 @@ void prefill_attention_kernel(const KernelArgs p) {
   const int2 tb = kv_tile_range(c, n, t, p.block_q, BN, p.causal, p.window_left,
                                 p.window_right, ranges, R);
 
-  const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int half = lane >> 5;
@@ -320,26 +419,118 @@ void prefill_attention_kernel(const KernelArgs p) {
   const int w_hi_max = __builtin_amdgcn_readfirstlane(wave_max(valid ? hi_a : INT_MIN));
   const bool wave_active = w_hi_max != INT_MIN;
 
-  // ---- gather: wave `wave` issues copies id = wave + q*NW of each tensor; a
-  // copy fills key rows [id*ROWS_PER_DMA, +ROWS_PER_DMA), lane -> (row, slot).
+  // ---- gather: wave `wave` issues copies id = wave*DMA_PER_WAVE + q of each
+  // tensor; copy id fills key rows [id*ROWS_PER_DMA, +ROWS_PER_DMA), lane ->
+  // (row, 16-byte slot).
   const uint32_t smem_base =
       __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u16*)&smem[0][0][0]);
   const int lane_row = lane / Lay::CHUNKS;
   const int lane_slot = lane % Lay::CHUNKS;
   const int64_t kv_row_stride = (int64_t)p.num_kv_heads * D;
   const int64_t lane_row_off = (int64_t)lane_row * kv_row_stride;
-  auto issue_tile = [&](int tile, int stage) {
+  // Wavefront `wave` fills tile rows [wave*WROWS, +WROWS) with DMA_PER_WAVE
+  // copies per tensor; byte offsets of this lane's 16 bytes from the first
+  // row's source, when those rows are consecutive in memory.
+  constexpr int WROWS = C::DMA_PER_WAVE * Lay::ROWS_PER_DMA;
+  // Source bases held in scalar registers (otherwise the compiler re-reads
+  // them from the argument block inside the loop to pick one).
+  const uint16_t* kc_ptr = p.k_cache;
+  const uint16_t* vc_ptr = p.v_cache;
+  const uint16_t* kn_ptr = p.k_new;
+  const uint16_t* vn_ptr = p.v_new;
+  const uint16_t* zero_row = g_zero_row;
+  asm volatile("" : "+s"(kc_ptr), "+s"(vc_ptr), "+s"(kn_ptr), "+s"(vn_ptr), "+s"(zero_row));
+  uint32_t voff_k[C::DMA_PER_WAVE], voff_v[C::DMA_PER_WAVE];
+#pragma unroll
+  for (int qi = 0; qi < C::DMA_PER_WAVE; ++qi) {
+    const int rr = qi * Lay::ROWS_PER_DMA + lane_row;  // row within the wavefront's rows
+    const int r = wave * WROWS + rr;                    // tile row
+    voff_k[qi] = (uint32_t)((rr * kv_row_stride + 8 * Lay::kslot(r, lane_slot)) * 2);
+    voff_v[qi] = (uint32_t)((rr * kv_row_stride + 8 * Lay::vslot(r, lane_slot)) * 2);
+  }
+  // Block-table entries of every page the tile loop reads, staged in LDS once,
+  // so the loop resolves pages with one LDS read per lane.  Workgroups that
+  // touch more than BT_CACHE pages fall back to scalar-unit block-table reads.
+  __shared__ int bt_cache[C::BT_CACHE];
+  const uint32_t page_magic = p.page_magic;
+  const int page_shift = p.page_shift;
+  const int cache_lo = tb.x * BN;
+  const int cache_hi = min(tb.y * BN, cache_end);
+  const int pg_base = cache_hi > cache_lo ? page_of(cache_lo, page_magic, page_shift) : 0;
+  const int pg_count = cache_hi > cache_lo ? page_of(cache_hi - 1, page_magic, page_shift) - pg_base + 1 : 0;
+  const bool bt_in_lds = pg_count <= C::BT_CACHE;
+  if (bt_in_lds) {
+    for (int i = tid; i < pg_count; i += C::THREADS) bt_cache[i] = bt[pg_base + i];
+  }
+  block_barrier();
+
+  auto issue_tile = [&](int tile, int stage) __attribute__((always_inline)) {
     const int j0 = tile * BN;
+    const uint32_t kst = smem_base + (uint32_t)(stage * 2 * TILE_ELEMS * 2);
+    const uint32_t vst = kst + (uint32_t)(TILE_ELEMS * 2);
+    const int ws = j0 + wave * WROWS;  // first key of this wavefront's rows
+    if (bt_in_lds) {
+      // Usual case, decided per wavefront: its WROWS keys are consecutive rows
+      // of one source (one cache page, or the new-token buffer).  The row base
+      // is then scalar and each lane adds its fixed offset.
+      const int pg = page_of(ws, page_magic, page_shift);
+      const int slot = ws - pg * p.page_size;
+      const uint16_t* kb = nullptr;
+      const uint16_t* vb = nullptr;
+      if (ws + WROWS <= cache_end && slot + WROWS <= p.page_size) {
+        const int page = __builtin_amdgcn_readfirstlane(bt_cache[pg - pg_base]);
+        const int64_t off = ((int64_t)page * p.page_size + slot) * kv_row_stride + (int64_t)g * D;
+        kb = kc_ptr + off;
+        vb = vc_ptr + off;
+      } else if (ws >= cache_end && ws + WROWS <= L) {
+        const int64_t off = (int64_t)(q0 + ws - c) * kv_row_stride + (int64_t)g * D;
+        kb = kn_ptr + off;
+        vb = vn_ptr + off;
+      }
+      if (kb != nullptr) {
+#pragma unroll
+        for (int qi = 0; qi < C::DMA_PER_WAVE; ++qi) {
+          const uint32_t dst = (uint32_t)((wave * C::DMA_PER_WAVE + qi) * 1024);
+          dma16s(voff_k[qi], kb, kst + dst);
+          dma16s(voff_v[qi], vb, vst + dst);
+        }
+        return;
+      }
+      // Otherwise per lane: cached position, new row, or past the end.
+#pragma unroll
+      for (int qi = 0; qi < C::DMA_PER_WAVE; ++qi) {
+        const int id = wave * C::DMA_PER_WAVE + qi;
+        const int r = id * Lay::ROWS_PER_DMA + lane_row;  // tile row of this lane
+        const int j = j0 + r;
+        const uint16_t* kp = zero_row;
+        const uint16_t* vp = zero_row;
+        if (j < cache_end) {
+          const int pgl = page_of(j, page_magic, page_shift);
+          const int slotl = j - pgl * p.page_size;
+          const int page = bt_cache[pgl - pg_base];
+          const int64_t off = ((int64_t)page * p.page_size + slotl) * kv_row_stride + (int64_t)g * D;
+          kp = p.k_cache + off;
+          vp = p.v_cache + off;
+        } else if (j < L) {
+          const int64_t off = (int64_t)(q0 + j - c) * kv_row_stride + (int64_t)g * D;
+          kp = p.k_new + off;
+          vp = p.v_new + off;
+        }
+        dma16(kp + 8 * Lay::kslot(r, lane_slot), kst + (uint32_t)(id * 1024));
+        dma16(vp + 8 * Lay::vslot(r, lane_slot), vst + (uint32_t)(id * 1024));
+      }
+      return;
+    }
 #pragma unroll
     for (int qi = 0; qi < C::DMA_PER_WAVE; ++qi) {
-      const int id = wave + qi * NW;
+      const int id = wave * C::DMA_PER_WAVE + qi;
       const int rbase = id * Lay::ROWS_PER_DMA;
       const int js = j0 + rbase;             // first key of this copy (wave-uniform)
       const int r = rbase + lane_row;         // tile row of this lane
       const int j = js + lane_row;
       const int je = js + Lay::ROWS_PER_DMA;  // one past the copy's last key
-      const uint16_t* kp = g_zero_row;
-      const uint16_t* vp = g_zero_row;
+      const uint16_t* kp = zero_row;
+      const uint16_t* vp = zero_row;
       // Common cases, decided per wave: every key of the copy in one cache
       // page, every key a new row, or every key past the sequence.  The row
       // base is then computed on the scalar unit.
@@ -380,23 +571,28 @@ void prefill_attention_kernel(const KernelArgs p) {
         kp = p.k_new + off;
         vp = p.v_new + off;
       }
-      const uint32_t kdst = smem_base + (uint32_t)((stage * 2 + 0) * TILE_ELEMS * 2 + id * 1024);
-      const uint32_t vdst = smem_base + (uint32_t)((stage * 2 + 1) * TILE_ELEMS * 2 + id * 1024);
-      dma16(kp + 8 * Lay::kslot(r, lane_slot), kdst);
-      dma16(vp + 8 * Lay::vslot(r, lane_slot), vdst);
+      dma16(kp + 8 * Lay::kslot(r, lane_slot), kst + (uint32_t)(id * 1024));
+      dma16(vp + 8 * Lay::vslot(r, lane_slot), vst + (uint32_t)(id * 1024));
     }
   };
 
   f32x16 oacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
-  // Reference max of scale*log2(e)*score used as the exp2 offset.  It only
-  // moves when a row's max grows by more than kLazy (factor 2^kLazy), so the
-  // O rescale is rare; the softmax is unchanged because numerator and
-  // denominator share the offset, and p <= 2^kLazy stays far from overflow.
-  // Starts finite so that fully masked entries give exp2(-inf) = 0.
+  // Scores are accumulated in log2 units (Q is prescaled by scale*log2(e))
+  // and relative to a per-row reference max m_run: the QK^T accumulators start
+  // at -m_run (minit), so p = exp2(acc) needs no further arithmetic.  m_run
+  // only moves when a row's max exceeds it by more than kLazy (factor
+  // 2^kLazy), so the O rescale is rare; numerator and denominator share the
+  // offset, and p <= 2^kLazy stays far from overflow.  A row's m_run is -inf
+  // until its first unmasked key; meanwhile its accumulators start at 0.
   constexpr float kLazy = 8.f;
-  float m_run = -1e30f;
+  float m_run = -INFINITY;
+  float mi = 0.f;           // -m_run once the row has one, else 0
+  // D = 256 has no registers to spare for the splatted start value; there the
+  // offset is added after the product instead.
+  constexpr bool kSplatInit = D <= 128;
+  f32x16 minit = {};        // mi in every element: QK^T accumulator start
   float l_run = 0.f;        // running row sum (this lane half's keys)
 
   // Lane-invariant LDS byte offsets of the operand reads (stage 0).
@@ -412,10 +608,14 @@ void prefill_attention_kernel(const KernelArgs p) {
                                                  16 * Lay::vslot(v_row_in, v_dim_in >> 3) +
                                                  2 * (v_dim_in & 7));
 
+  // Ring protocol (NSTAGE = 4): the copies of tile i + 2 are issued at the top
+  // of iteration i, into the stage of tile i - 2, which every wavefront
+  // released before passing the previous iteration's barrier.  Two tiles are
+  // in flight while one is waited for.
+  static_assert(NSTAGE == 4, "ring protocol assumes four stages");
   const int ntile = tb.y - tb.x;
-#pragma unroll
-  for (int i = 0; i < NSTAGE - 1; ++i)
-    if (i < ntile) issue_tile(tb.x + i, i);
+  if (ntile > 0) issue_tile(tb.x, 0);
+  if (ntile > 1) issue_tile(tb.x + 1, 1);
 
   // ---- Q fragments: B operand of S^T = K Q^T (lane: row `col`, dims 16ks + 8half..+8)
   bf16x8 qf[KSTEPS];
@@ -424,7 +624,8 @@ void prefill_attention_kernel(const KernelArgs p) {
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       u32x4 v = valid ? *(const u32x4*)(qrow + 16 * ks + 8 * half) : u32x4{0, 0, 0, 0};
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
+      const f32x8 x = __builtin_convertvector(__builtin_bit_cast(bf16x8, v), f32x8);
+      qf[ks] = __builtin_convertvector(x * p.scale_log2, bf16x8);
     }
   }
   // The Q loads must be complete before the tile loop, or the compiler places
@@ -433,34 +634,55 @@ void prefill_attention_kernel(const KernelArgs p) {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
 
-  for (int it = 0; it < ntile; ++it) {
-    // copies of this tile are done once at most `after` later tiles are in flight
-    wait_copies<2 * C::DMA_PER_WAVE, NSTAGE - 2>(ntile - 1 - it);
-    block_barrier();
-    if (it + NSTAGE - 1 < ntile) issue_tile(tb.x + it + NSTAGE - 1, (it + NSTAGE - 1) % NSTAGE);
-
-    const int stage = it % NSTAGE;
+  // ---- per-tile pieces
+  auto tile_active = [&](int it) __attribute__((always_inline)) {
     const int j0 = (tb.x + it) * BN;
-    if (!wave_active || j0 > w_hi_max || j0 + BN - 1 < w_lo_min) continue;
-    const bool interior = j0 >= w_lo_max && j0 + BN - 1 <= w_hi_min;
-
-    // S^T[key][query] = K Q^T
-    f32x16 sacc[NKB];
+    return wave_active && j0 <= w_hi_max && j0 + BN - 1 >= w_lo_min;
+  };
+  // S^T[key][query] = K Q^T; accumulator element r of block kb holds key
+  // j0 + 32kb + 8(r/4) + 4half + r%4 for this lane's query row.
+  // k-step outer, key block inner: consecutive MFMAs are independent, and the
+  // fragments of step ks+1 are read before the MFMAs of step ks are issued.
+  auto qk = [&](int stage, f32x16* sacc) __attribute__((always_inline)) {
     uint32_t kbase = k_lane + (uint32_t)(stage * 2 * TILE_ELEMS * 2);
     asm volatile("" : "+v"(kbase));  // keep the per-read XORs in the loop (no hoisting)
+    auto kfrag = [&](int kb, int ks) __attribute__((always_inline)) {
+      const uint32_t addr = (kbase + (uint32_t)(kb * 32 * D * 2)) ^ (uint32_t)(32 * ks);
+      return *(const lds_u32x4*)(uintptr_t)addr;
+    };
+    // Fragment i = (k-step i / NKB, key block i % NKB).  Reads run QK_DEPTH
+    // fragments ahead of the MFMA that consumes them, so LDS latency overlaps
+    // the matrix pipe; the scheduling barriers keep the compiler from sinking
+    // the reads next to their uses.
+    constexpr int NF = KSTEPS * NKB;
+    constexpr int PD = QK_DEPTH < NF ? QK_DEPTH : NF;
+    u32x4 fr[PD];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      sacc[kb] = f32x16{};
+    for (int i = 0; i < PD; ++i) fr[i] = kfrag(i % NKB, i / NKB);
+    __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const uint32_t addr = (kbase + (uint32_t)(kb * 32 * D * 2)) ^ (uint32_t)(32 * ks);
-        const u32x4 a = *(const lds_u32x4*)(uintptr_t)addr;
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                          qf[ks], sacc[kb], 0, 0, 0);
-      }
+    for (int i = 0; i < NF; ++i) {
+      const u32x4 a = fr[i % PD];
+      if (i + PD < NF) fr[i % PD] = kfrag((i + PD) % NKB, (i + PD) / NKB);
+      sacc[i % NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8, a), qf[i / NKB],
+          i < NKB ? (kSplatInit ? minit : f32x16{}) : sacc[i % NKB], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + PD < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    // accumulator element r of block kb holds key j0 + 32kb + 8(r/4) + 4half + r%4
+    if constexpr (!kSplatInit) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] += mi;
+    }
+  };
+  // Element mask (boundary tiles only), row max, lazy rescale of O and l.
+  auto mask_rowmax = [&](int it, f32x16* sacc) __attribute__((always_inline)) {
+    const int j0 = (tb.x + it) * BN;
+    const bool interior = j0 >= w_lo_max && j0 + BN - 1 <= w_hi_min;
     if (!interior) {
+      asm volatile("");  // keep this a branch: interior tiles skip the mask
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -474,30 +696,39 @@ void prefill_attention_kernel(const KernelArgs p) {
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = pair_max(mx) * p.scale_log2;
-    const bool grow = mx > m_run + kLazy;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform branch
-      const float m_new = grow ? mx : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    mx = pair_max(mx);  // row max relative to the reference
+    const bool unset = m_run == -INFINITY;
+    const bool adj = unset ? mx > -INFINITY : mx > kLazy;
+    if (__builtin_amdgcn_ballot_w64(adj) != 0) {  // wave-uniform branch
+      asm volatile("");  // keep this a branch: it is taken rarely
+      const float d = adj ? mx : 0.f;
+      const float alpha = unset ? 1.f : __builtin_amdgcn_exp2f(-d);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      m_run = m_new;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] -= d;
+      m_run = unset ? (adj ? mx : m_run) : m_run + d;
+      mi = m_run == -INFINITY ? 0.f : -m_run;
+      if constexpr (kSplatInit) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) minit[r] = mi;
+      }
     }
-    float rs = 0.f;
+  };
+  // p = exp2(scale*log2(e)*s - m), row sum, and P^T as bf16 B operands
+  // (PV step ks2 covers keys 16ks2..16ks2+15).
+  auto expsum = [&](f32x16* sacc, bf16x8* pf) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][r], p.scale_log2, -m_run));
-        sacc[kb][r] = e;
-        rs += e;
-      }
-    l_run += rs;
-    // P^T as B operands: PV step ks2 covers keys 16ks2..16ks2+15
-    bf16x8 pf[PSTEPS];
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = __builtin_amdgcn_exp2f(sacc[kb][r]);
+    // The row sum adds the bf16-rounded p that the PV product uses.
+    const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
     for (int ks2 = 0; ks2 < PSTEPS; ++ks2) {
       const f32x8 v = {sacc[ks2 >> 1][8 * (ks2 & 1) + 0], sacc[ks2 >> 1][8 * (ks2 & 1) + 1],
@@ -505,25 +736,58 @@ void prefill_attention_kernel(const KernelArgs p) {
                        sacc[ks2 >> 1][8 * (ks2 & 1) + 4], sacc[ks2 >> 1][8 * (ks2 & 1) + 5],
                        sacc[ks2 >> 1][8 * (ks2 & 1) + 6], sacc[ks2 >> 1][8 * (ks2 & 1) + 7]};
       pf[ks2] = __builtin_convertvector(v, bf16x8);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[ks2], pf[ks2], 0, 1), ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[ks2], pf[ks2], 2, 3), ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[ks2], pf[ks2], 4, 5), ones, l_run, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[ks2], pf[ks2], 6, 7), ones, l_run, false);
     }
-    // O^T[dim][query] += V^T P^T.  A element e holds key 16ks2 + 8(e/4) + 4half + e%4 at
-    // dim 32db + col: two transpose reads of 4 keys x 16 dims per 16-lane group.
+  };
+  // O^T[dim][query] += V^T P^T.  A element e holds key 16ks2 + 8(e/4) + 4half + e%4 at
+  // dim 32db + col: two transpose reads of 4 keys x 16 dims per 16-lane group.
+  // Key step outer, dim block inner: consecutive MFMAs are independent; the
+  // fragments of the next (ks2, db) pair are read one MFMA ahead.
+  auto pv = [&](int stage, const bf16x8* pf) __attribute__((always_inline)) {
     uint32_t vbase = v_lane + (uint32_t)((stage * 2 + 1) * TILE_ELEMS * 2);
     asm volatile("" : "+v"(vbase));
+    auto vfrag = [&](int ks2, int db) __attribute__((always_inline)) {
+      const uint32_t a0 = (vbase ^ (uint32_t)(64 * db)) + (uint32_t)(16 * ks2 * 2 * D);
+      const uint32_t a1 = a0 + (uint32_t)(8 * 2 * D);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a0);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a1);
+      const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+      const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+      return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+    };
+    // Fragment i = (key step i / NDB, dim block i % NDB), PV_DEPTH ahead.
+    constexpr int NV = PSTEPS * NDB;
+    constexpr int PD = PV_DEPTH < NV ? PV_DEPTH : NV;
+    u32x4 fr[PD];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int i = 0; i < PD; ++i) fr[i] = vfrag(i / NDB, i % NDB);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PD, 0);
 #pragma unroll
-      for (int ks2 = 0; ks2 < PSTEPS; ++ks2) {
-        const uint32_t a0 = (vbase ^ (uint32_t)(64 * db)) + (uint32_t)(16 * ks2 * 2 * D);
-        const uint32_t a1 = a0 + (uint32_t)(8 * 2 * D);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a0);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)a1);
-        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-        const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
-        const u32x4 a = {lo2[0], lo2[1], hi2[0], hi2[1]};
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                          pf[ks2], oacc[db], 0, 0, 0);
-      }
+    for (int i = 0; i < NV; ++i) {
+      const u32x4 a = fr[i % PD];
+      if (i + PD < NV) fr[i % PD] = vfrag((i + PD) / NDB, (i + PD) % NDB);
+      oacc[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                             pf[i / NDB], oacc[i % NDB], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + PD < NV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  };
+
+  // One tile at a time: refill, wait for this tile's copies, publish, compute.
+  for (int it = 0; it < ntile; ++it) {
+    if (it + 2 < ntile) issue_tile(tb.x + it + 2, (it + 2) % NSTAGE);
+    wait_copies<2 * C::DMA_PER_WAVE, 2>(ntile - 1 - it);
+    block_barrier();
+    if (!tile_active(it)) continue;
+    f32x16 sacc[NKB];
+    bf16x8 pf[PSTEPS];
+    qk(it % NSTAGE, sacc);
+    mask_rowmax(it, sacc);
+    expsum(sacc, pf);
+    pv(it % NSTAGE, pf);
   }
 
   // ---- epilogue: O / l -> bf16; lane holds dims 32db + 8(r/4) + 4half + r%4
@@ -738,7 +1002,12 @@ int prefill_attention(const void* q, const void* k_new, const void* v_new,
   a.cache_only = k_new == nullptr ? 1 : 0;
 
   const int64_t num_q_tiles = ((int64_t)max_q_len + tc.block_q - 1) / tc.block_q;
-  const int64_t grid = num_q_tiles * num_seqs * num_kv_heads * a.head_blocks;
+  a.num_q_tiles = (int32_t)num_q_tiles;
+  // slots per XCD: every group an XCD can own, each with up to num_q_tiles tiles
+  const int64_t groups_per_xcd = num_seqs <= kSortMaxSeqs
+      ? (int64_t)num_seqs * ((num_kv_heads + kNumXcd - 1) / kNumXcd)
+      : ((int64_t)num_seqs * num_kv_heads + kNumXcd - 1) / kNumXcd;
+  const int64_t grid = kNumXcd * groups_per_xcd * num_q_tiles * a.head_blocks;
   if (grid > 0x7fffffff) return PAGED_PREFILL_ERR_UNSUPPORTED;
   hipError_t err;
   switch (head_size) {
