@@ -53,17 +53,17 @@ constexpr int kMaxMmRanges = 4096;
 constexpr int kNumXcd = 8;         // MI355X: 8 accelerator complex dies, one L2 each
 constexpr int kSortMaxSeqs = 256;  // batches up to this size get heavy-first ordering
 
-// Tile shape per head size: wavefronts per workgroup (32 query rows each), keys
-// per KV tile, depth of the LDS ring, and wavefronts per SIMD.  Overridable at
-// build time (-DPREFILL_TILE_D128=4,32,4,2) for tile-shape sweeps.
+// Tile shape per head size: wavefronts per workgroup, keys per KV tile, depth
+// of the LDS ring, wavefronts per SIMD, and 32-row query blocks per wavefront.
+// Overridable at build time (-DPREFILL_TILE_D128=4,64,4,1,2) for sweeps.
 #ifndef PREFILL_TILE_D64
-#define PREFILL_TILE_D64 4, 64, 4, 2
+#define PREFILL_TILE_D64 4, 64, 4, 2, 1
 #endif
 #ifndef PREFILL_TILE_D128
-#define PREFILL_TILE_D128 8, 64, 4, 2
+#define PREFILL_TILE_D128 8, 64, 4, 2, 1
 #endif
 #ifndef PREFILL_TILE_D256
-#define PREFILL_TILE_D256 8, 32, 4, 2
+#define PREFILL_TILE_D256 8, 32, 4, 2, 1
 #endif
 
 // Rows past the end of a sequence are gathered from here: exact zeros.
@@ -319,15 +319,16 @@ __device__ WorkItem decode_work(const Args& p, int b, int tid, int nthreads, int
   return w;
 }
 
-template <int D_, int NW_, int BN_, int NSTAGE_, int WPE_>
+template <int D_, int NW_, int BN_, int NSTAGE_, int WPE_, int RB_>
 struct TileShape {
   static constexpr int D = D_;
   static constexpr int NW = NW_;
   static constexpr int BN = BN_;          // keys per KV tile
   static constexpr int NSTAGE = NSTAGE_;  // LDS ring depth (NSTAGE - 1 tiles in flight)
   static constexpr int WPE = WPE_;        // wavefronts per SIMD
+  static constexpr int RB = RB_;          // 32-row query blocks per wavefront
   static constexpr int THREADS = 64 * NW;
-  static constexpr int ROWS = 32 * NW;
+  static constexpr int ROWS = 32 * RB * NW;
   static constexpr int DMA_PER_TENSOR = BN * D * 2 / 1024;  // 1-KB copies per tile per tensor
   static constexpr int DMA_PER_WAVE = DMA_PER_TENSOR / NW;
   static constexpr int LDS_BYTES = NSTAGE * 2 * BN * D * 2;
@@ -365,14 +366,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(C::THREADS, C::THREADS),
 void prefill_attention_kernel(const KernelArgs p) {
   constexpr int D = C::D;
   constexpr int NW = C::NW;
+  constexpr int RB = C::RB;
   constexpr int NSTAGE = C::NSTAGE;
   using Lay = TileLayout<D>;
   constexpr int BN = C::BN;
   constexpr int KSTEPS = D / 16;   // QK^T contraction steps of 16 dims
   constexpr int NKB = BN / 32;     // 32-key blocks per KV tile
   constexpr int PSTEPS = BN / 16;  // PV contraction steps of 16 keys
-  constexpr int QK_DEPTH = 4;      // K fragments in flight ahead of the QK MFMAs
-  constexpr int PV_DEPTH = 3;      // V fragments in flight ahead of the PV MFMAs
+  // Operand fragments in flight ahead of the MFMAs that consume them (each
+  // fragment feeds RB MFMAs).
+  constexpr int QK_DEPTH = RB == 1 ? 4 : 3;
+  constexpr int PV_DEPTH = RB == 1 ? 3 : 2;
   constexpr int NDB = D / 32;      // 32-dim blocks of the output
   constexpr int TILE_ELEMS = BN * D;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[NSTAGE][2][TILE_ELEMS];
@@ -403,20 +407,34 @@ void prefill_attention_kernel(const KernelArgs p) {
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  // ---- this lane's query row (both lane halves hold the same row)
-  const int row = wave * 32 + col;
-  const int hb = row / p.block_q;
-  const int tok = t * p.block_q + (row - hb * p.block_q);
-  const bool valid = tok < n;
-  const int head = g * p.group + hblk * p.heads_per_tile + hb;
-  int lo_a = 1, hi_a = 0;
-  if (valid)
-    row_interval(c + tok, L, p.causal, p.window_left, p.window_right, ranges, R, lo_a, hi_a);
+  // ---- this lane's query rows, one per row block (both lane halves hold the
+  // same rows): tile row wave*32*RB + 32*rb + col
+  int tok[RB], head[RB], lo_a[RB], hi_a[RB];
+  bool valid[RB];
+  int lo_max = INT_MIN, hi_min = INT_MAX, lo_min = INT_MAX, hi_max = INT_MIN;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = (wave * RB + rb) * 32 + col;
+    const int hb = row / p.block_q;
+    tok[rb] = t * p.block_q + (row - hb * p.block_q);
+    valid[rb] = tok[rb] < n;
+    head[rb] = g * p.group + hblk * p.heads_per_tile + hb;
+    lo_a[rb] = 1;
+    hi_a[rb] = 0;
+    if (valid[rb]) {
+      row_interval(c + tok[rb], L, p.causal, p.window_left, p.window_right, ranges, R,
+                   lo_a[rb], hi_a[rb]);
+      lo_max = max(lo_max, lo_a[rb]);
+      hi_min = min(hi_min, hi_a[rb]);
+      lo_min = min(lo_min, lo_a[rb]);
+      hi_max = max(hi_max, hi_a[rb]);
+    }
+  }
   // wave-uniform summaries of the rows' key intervals (scalar registers)
-  const int w_lo_max = __builtin_amdgcn_readfirstlane(wave_max(valid ? lo_a : INT_MIN));
-  const int w_hi_min = __builtin_amdgcn_readfirstlane(wave_min(valid ? hi_a : INT_MAX));
-  const int w_lo_min = __builtin_amdgcn_readfirstlane(wave_min(valid ? lo_a : INT_MAX));
-  const int w_hi_max = __builtin_amdgcn_readfirstlane(wave_max(valid ? hi_a : INT_MIN));
+  const int w_lo_max = __builtin_amdgcn_readfirstlane(wave_max(lo_max));
+  const int w_hi_min = __builtin_amdgcn_readfirstlane(wave_min(hi_min));
+  const int w_lo_min = __builtin_amdgcn_readfirstlane(wave_min(lo_min));
+  const int w_hi_max = __builtin_amdgcn_readfirstlane(wave_max(hi_max));
   const bool wave_active = w_hi_max != INT_MIN;
 
   // ---- gather: wave `wave` issues copies id = wave*DMA_PER_WAVE + q of each
@@ -576,9 +594,11 @@ void prefill_attention_kernel(const KernelArgs p) {
     }
   };
 
-  f32x16 oacc[NDB];
+  f32x16 oacc[RB][NDB];
 #pragma unroll
-  for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) oacc[rb][i] = f32x16{};
   // Scores are accumulated in log2 units (Q is prescaled by scale*log2(e))
   // and relative to a per-row reference max m_run: the QK^T accumulators start
   // at -m_run (minit), so p = exp2(acc) needs no further arithmetic.  m_run
@@ -587,13 +607,18 @@ void prefill_attention_kernel(const KernelArgs p) {
   // offset, and p <= 2^kLazy stays far from overflow.  A row's m_run is -inf
   // until its first unmasked key; meanwhile its accumulators start at 0.
   constexpr float kLazy = 8.f;
-  float m_run = -INFINITY;
-  float mi = 0.f;           // -m_run once the row has one, else 0
-  // D = 256 has no registers to spare for the splatted start value; there the
-  // offset is added after the product instead.
-  constexpr bool kSplatInit = D <= 128;
-  f32x16 minit = {};        // mi in every element: QK^T accumulator start
-  float l_run = 0.f;        // running row sum (this lane half's keys)
+  float m_run[RB], mi[RB], l_run[RB];  // mi = -m_run once the row has one, else 0
+  // Without registers to spare for the splatted start value (D = 256, or two
+  // row blocks) the offset is added after the product instead.
+  constexpr bool kSplatInit = D <= 128 && RB == 1;
+  f32x16 minit[RB];                    // mi in every element: QK^T accumulator start
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_run[rb] = -INFINITY;
+    mi[rb] = 0.f;
+    l_run[rb] = 0.f;                   // running row sum (this lane half's keys)
+    minit[rb] = f32x16{};
+  }
 
   // Lane-invariant LDS byte offsets of the operand reads (stage 0).
   // K (A operand of S^T): row `col` of each 32-key block, chunk 2ks + half.
@@ -618,14 +643,16 @@ void prefill_attention_kernel(const KernelArgs p) {
   if (ntile > 1) issue_tile(tb.x + 1, 1);
 
   // ---- Q fragments: B operand of S^T = K Q^T (lane: row `col`, dims 16ks + 8half..+8)
-  bf16x8 qf[KSTEPS];
-  {
-    const uint16_t* qrow = p.q + ((int64_t)(q0 + (valid ? tok : 0)) * p.num_heads + head) * D;
+  bf16x8 qf[RB][KSTEPS];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const uint16_t* qrow =
+        p.q + ((int64_t)(q0 + (valid[rb] ? tok[rb] : 0)) * p.num_heads + head[rb]) * D;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      u32x4 v = valid ? *(const u32x4*)(qrow + 16 * ks + 8 * half) : u32x4{0, 0, 0, 0};
+      u32x4 v = valid[rb] ? *(const u32x4*)(qrow + 16 * ks + 8 * half) : u32x4{0, 0, 0, 0};
       const f32x8 x = __builtin_convertvector(__builtin_bit_cast(bf16x8, v), f32x8);
-      qf[ks] = __builtin_convertvector(x * p.scale_log2, bf16x8);
+      qf[rb][ks] = __builtin_convertvector(x * p.scale_log2, bf16x8);
     }
   }
   // The Q loads must be complete before the tile loop, or the compiler places
@@ -643,7 +670,7 @@ void prefill_attention_kernel(const KernelArgs p) {
   // j0 + 32kb + 8(r/4) + 4half + r%4 for this lane's query row.
   // k-step outer, key block inner: consecutive MFMAs are independent, and the
   // fragments of step ks+1 are read before the MFMAs of step ks are issued.
-  auto qk = [&](int stage, f32x16* sacc) __attribute__((always_inline)) {
+  auto qk = [&](int stage, f32x16 (*sacc)[NKB]) __attribute__((always_inline)) {
     uint32_t kbase = k_lane + (uint32_t)(stage * 2 * TILE_ELEMS * 2);
     asm volatile("" : "+v"(kbase));  // keep the per-read XORs in the loop (no hoisting)
     auto kfrag = [&](int kb, int ks) __attribute__((always_inline)) {
@@ -664,89 +691,120 @@ void prefill_attention_kernel(const KernelArgs p) {
     for (int i = 0; i < NF; ++i) {
       const u32x4 a = fr[i % PD];
       if (i + PD < NF) fr[i % PD] = kfrag((i + PD) % NKB, (i + PD) / NKB);
-      sacc[i % NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          __builtin_bit_cast(bf16x8, a), qf[i / NKB],
-          i < NKB ? (kSplatInit ? minit : f32x16{}) : sacc[i % NKB], 0, 0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        sacc[rb][i % NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, a), qf[rb][i / NKB],
+            i < NKB ? (kSplatInit ? minit[rb] : f32x16{}) : sacc[rb][i % NKB], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
       if (i + PD < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     if constexpr (!kSplatInit) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] += mi;
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[rb][kb][r] += mi[rb];
     }
   };
   // Element mask (boundary tiles only), row max, lazy rescale of O and l.
-  auto mask_rowmax = [&](int it, f32x16* sacc) __attribute__((always_inline)) {
+  auto mask_rowmax = [&](int it, f32x16 (*sacc)[NKB]) __attribute__((always_inline)) {
     const int j0 = (tb.x + it) * BN;
     const bool interior = j0 >= w_lo_max && j0 + BN - 1 <= w_hi_min;
     if (!interior) {
       asm volatile("");  // keep this a branch: interior tiles skip the mask
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int rb = 0; rb < RB; ++rb) {
+        // element (kb, r) holds key j0 + 4half + o with o = 32kb + 8(r/4) + r%4;
+        // it is allowed iff (unsigned)(o - lo) <= (unsigned)(hi - lo), relative
+        // to this lane's keys.
+        const int lo = lo_a[rb] - j0 - 4 * half;
+        const uint32_t width = (uint32_t)(hi_a[rb] - lo_a[rb]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + kb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (key < lo_a || key > hi_a) sacc[kb][r] = -INFINITY;
-        }
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int o = kb * 32 + 8 * (r >> 2) + (r & 3);
+            float v = sacc[rb][kb][r];
+            v = (uint32_t)(o - lo) <= width ? v : -INFINITY;
+            asm volatile("" : "+v"(v));
+            sacc[rb][kb][r] = v;
+          }
+      }
     }
-    float mx = -INFINITY;
+    float mx[RB];
+    bool adj[RB];
+    bool any_adj = false;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = pair_max(mx);  // row max relative to the reference
-    const bool unset = m_run == -INFINITY;
-    const bool adj = unset ? mx > -INFINITY : mx > kLazy;
-    if (__builtin_amdgcn_ballot_w64(adj) != 0) {  // wave-uniform branch
-      asm volatile("");  // keep this a branch: it is taken rarely
-      const float d = adj ? mx : 0.f;
-      const float alpha = unset ? 1.f : __builtin_amdgcn_exp2f(-d);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    for (int rb = 0; rb < RB; ++rb) {
+      float m = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] -= d;
-      m_run = unset ? (adj ? mx : m_run) : m_run + d;
-      mi = m_run == -INFINITY ? 0.f : -m_run;
-      if constexpr (kSplatInit) {
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, sacc[rb][kb][r]);
+      mx[rb] = pair_max(m);  // row max relative to the reference
+      adj[rb] = m_run[rb] == -INFINITY ? mx[rb] > -INFINITY : mx[rb] > kLazy;
+      any_adj |= adj[rb];
+    }
+    if (__builtin_amdgcn_ballot_w64(any_adj) != 0) {  // wave-uniform branch
+      asm volatile("");  // keep this a branch: it is taken rarely
 #pragma unroll
-        for (int r = 0; r < 16; ++r) minit[r] = mi;
+      for (int rb = 0; rb < RB; ++rb) {
+        const bool unset = m_run[rb] == -INFINITY;
+        const float d = adj[rb] ? mx[rb] : 0.f;
+        const float alpha = unset ? 1.f : __builtin_amdgcn_exp2f(-d);
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[rb][kb][r] -= d;
+        m_run[rb] = unset ? (adj[rb] ? mx[rb] : m_run[rb]) : m_run[rb] + d;
+        mi[rb] = m_run[rb] == -INFINITY ? 0.f : -m_run[rb];
+        if constexpr (kSplatInit) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) minit[rb][r] = mi[rb];
+        }
       }
     }
   };
   // p = exp2(scale*log2(e)*s - m), row sum, and P^T as bf16 B operands
   // (PV step ks2 covers keys 16ks2..16ks2+15).
-  auto expsum = [&](f32x16* sacc, bf16x8* pf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = __builtin_amdgcn_exp2f(sacc[kb][r]);
+  auto expsum = [&](f32x16 (*sacc)[NKB], bf16x8 (*pf)[PSTEPS]) __attribute__((always_inline)) {
     // The row sum adds the bf16-rounded p that the PV product uses.
     const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
-    for (int ks2 = 0; ks2 < PSTEPS; ++ks2) {
-      const f32x8 v = {sacc[ks2 >> 1][8 * (ks2 & 1) + 0], sacc[ks2 >> 1][8 * (ks2 & 1) + 1],
-                       sacc[ks2 >> 1][8 * (ks2 & 1) + 2], sacc[ks2 >> 1][8 * (ks2 & 1) + 3],
-                       sacc[ks2 >> 1][8 * (ks2 & 1) + 4], sacc[ks2 >> 1][8 * (ks2 & 1) + 5],
-                       sacc[ks2 >> 1][8 * (ks2 & 1) + 6], sacc[ks2 >> 1][8 * (ks2 & 1) + 7]};
-      pf[ks2] = __builtin_convertvector(v, bf16x8);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[ks2], pf[ks2], 0, 1), ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[ks2], pf[ks2], 2, 3), ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[ks2], pf[ks2], 4, 5), ones, l_run, false);
-      l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pf[ks2], pf[ks2], 6, 7), ones, l_run, false);
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[rb][kb][r] = __builtin_amdgcn_exp2f(sacc[rb][kb][r]);
+#pragma unroll
+      for (int ks2 = 0; ks2 < PSTEPS; ++ks2) {
+        const f32x16& sv = sacc[rb][ks2 >> 1];
+        const int o = 8 * (ks2 & 1);
+        const f32x8 v = {sv[o + 0], sv[o + 1], sv[o + 2], sv[o + 3],
+                         sv[o + 4], sv[o + 5], sv[o + 6], sv[o + 7]};
+        const bf16x8 b = __builtin_convertvector(v, bf16x8);
+        pf[rb][ks2] = b;
+        float l = l_run[rb];
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 0, 1), ones, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 2, 3), ones, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 4, 5), ones, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(b, b, 6, 7), ones, l, false);
+        l_run[rb] = l;
+      }
     }
   };
   // O^T[dim][query] += V^T P^T.  A element e holds key 16ks2 + 8(e/4) + 4half + e%4 at
   // dim 32db + col: two transpose reads of 4 keys x 16 dims per 16-lane group.
   // Key step outer, dim block inner: consecutive MFMAs are independent; the
   // fragments of the next (ks2, db) pair are read one MFMA ahead.
-  auto pv = [&](int stage, const bf16x8* pf) __attribute__((always_inline)) {
+  auto pv = [&](int stage, const bf16x8 (*pf)[PSTEPS]) __attribute__((always_inline)) {
     uint32_t vbase = v_lane + (uint32_t)((stage * 2 + 1) * TILE_ELEMS * 2);
     asm volatile("" : "+v"(vbase));
     auto vfrag = [&](int ks2, int db) __attribute__((always_inline)) {
@@ -769,9 +827,11 @@ void prefill_attention_kernel(const KernelArgs p) {
     for (int i = 0; i < NV; ++i) {
       const u32x4 a = fr[i % PD];
       if (i + PD < NV) fr[i % PD] = vfrag((i + PD) / NDB, (i + PD) % NDB);
-      oacc[i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                             pf[i / NDB], oacc[i % NDB], 0, 0, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        oacc[rb][i % NDB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, a), pf[rb][i / NDB], oacc[rb][i % NDB], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
       if (i + PD < NV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
@@ -782,8 +842,8 @@ void prefill_attention_kernel(const KernelArgs p) {
     wait_copies<2 * C::DMA_PER_WAVE, 2>(ntile - 1 - it);
     block_barrier();
     if (!tile_active(it)) continue;
-    f32x16 sacc[NKB];
-    bf16x8 pf[PSTEPS];
+    f32x16 sacc[RB][NKB];
+    bf16x8 pf[RB][PSTEPS];
     qk(it % NSTAGE, sacc);
     mask_rowmax(it, sacc);
     expsum(sacc, pf);
@@ -791,19 +851,23 @@ void prefill_attention_kernel(const KernelArgs p) {
   }
 
   // ---- epilogue: O / l -> bf16; lane holds dims 32db + 8(r/4) + 4half + r%4
-  const float l_tot = pair_sum(l_run);
-  if (valid) {
-    const float inv = 1.f / l_tot;
-    uint16_t* orow = p.out + ((int64_t)(q0 + tok) * p.num_heads + head) * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int rb = 0; rb < RB; ++rb) {
+    const float l_tot = pair_sum(l_run[rb]);
+    if (valid[rb]) {
+      const float inv = 1.f / l_tot;
+      uint16_t* orow = p.out + ((int64_t)(q0 + tok[rb]) * p.num_heads + head[rb]) * D;
 #pragma unroll
-      for (int b4 = 0; b4 < 4; ++b4) {
-        const f32x4 v = {oacc[db][4 * b4] * inv, oacc[db][4 * b4 + 1] * inv,
-                         oacc[db][4 * b4 + 2] * inv, oacc[db][4 * b4 + 3] * inv};
-        const bf16x4 h = __builtin_convertvector(v, bf16x4);
-        *(u32x2*)(orow + db * 32 + 8 * b4 + 4 * half) = __builtin_bit_cast(u32x2, h);
-      }
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int b4 = 0; b4 < 4; ++b4) {
+          const f32x16& o = oacc[rb][db];
+          const f32x4 v = {o[4 * b4] * inv, o[4 * b4 + 1] * inv, o[4 * b4 + 2] * inv,
+                           o[4 * b4 + 3] * inv};
+          const bf16x4 h = __builtin_convertvector(v, bf16x4);
+          *(u32x2*)(orow + db * 32 + 8 * b4 + 4 * half) = __builtin_bit_cast(u32x2, h);
+        }
+    }
   }
 }
 
@@ -844,8 +908,8 @@ int gcd_int(int a, int b) {
 
 // Wavefronts per workgroup: 8 (two per SIMD) while the per-lane state fits 256
 // registers, 4 (one per SIMD, 512 registers) for head size 256.
-template <int D> void shape_of(int* nw, int* bn) {
-  *nw = ShapeFor<D>::T::NW;
+template <int D> void shape_of(int* rows, int* bn) {
+  *rows = ShapeFor<D>::T::ROWS;
   *bn = ShapeFor<D>::T::BN;
 }
 
@@ -854,11 +918,10 @@ int choose_tiles(int head_size, int num_heads, int num_kv_heads, TileChoice* tc)
     return PAGED_PREFILL_ERR_INVALID_ARG;
   if (head_size != 64 && head_size != 128 && head_size != 256)
     return PAGED_PREFILL_ERR_UNSUPPORTED;
-  int nw, bn;
-  if (head_size == 64) shape_of<64>(&nw, &bn);
-  else if (head_size == 128) shape_of<128>(&nw, &bn);
-  else shape_of<256>(&nw, &bn);
-  const int rows = 32 * nw;
+  int rows, bn;
+  if (head_size == 64) shape_of<64>(&rows, &bn);
+  else if (head_size == 128) shape_of<128>(&rows, &bn);
+  else shape_of<256>(&rows, &bn);
   const int group = num_heads / num_kv_heads;
   const int hpt = gcd_int(group, rows);  // heads of one group that share a tile
   tc->block_n = bn;
