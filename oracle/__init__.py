@@ -20,6 +20,10 @@ computes, written from the pages' definitions:
   report ("Key source snippets", compute_tile_loop_bounds).
 * ``bounds.useful_pairs`` — the number of allowed (query, key) pairs, which
   prices useful work at 4 * head_size FLOP per pair per query head.
+* mask variants (chunked local attention, a causal flag per sequence,
+  unclamped multimodal ranges) and ``attention.merge_partials``, the
+  log-sum-exp merge of split-KV segments.  Source: vLLM PR #53147 report
+  ("Key source snippets", compute_tile_loop_bounds; "Review highlights").
 
 Precision: fp32, as the pages' reference is fp32.  The oracle never rounds
 intermediates to bf16.  It shares no code with the HIP path and imports only
@@ -35,6 +39,7 @@ PR #53147 report.
 from .attention import (  # noqa: F401
     allowed_mask,
     gather_kv,
+    merge_partials,
     reference_prefill,
     reference_rows,
 )

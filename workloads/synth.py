@@ -77,6 +77,19 @@ class Workload:
     new_in_cache: bool = False
     seed: int = 0
     table_seed: int = 0
+    causal_per_seq: Optional[np.ndarray] = None  # int32 [S] 0/1; overrides ``causal``
+    mm_clamp: bool = True         # multimodal ranges clamped by window_left
+    chunk_size: int = 0           # chunked local attention when > 0 ...
+    chunk_lookback: int = -1      # ... and >= 0
+
+    @property
+    def causal_arg(self):
+        """The causal setting as the oracle takes it: one flag, or one per sequence."""
+        return self.causal if self.causal_per_seq is None else self.causal_per_seq
+
+    def mask_kwargs(self) -> dict:
+        return dict(chunk_size=self.chunk_size, chunk_lookback=self.chunk_lookback,
+                    mm_clamp=self.mm_clamp)
 
     @property
     def num_seqs(self) -> int:
@@ -121,7 +134,9 @@ def make_workload(*, seed: int, table_seed: Optional[int] = None, ctx_lens, q_le
                   mm_ranges=None, scale: Optional[float] = None,
                   spare_frac: float = 0.1, new_in_cache: bool = False,
                   block_table_override=None, name: str = "custom",
-                  rng: Optional[np.random.Generator] = None) -> Workload:
+                  rng: Optional[np.random.Generator] = None, causal_per_seq=None,
+                  mm_clamp: bool = True, chunk_size: int = 0,
+                  chunk_lookback: int = -1) -> Workload:
     """Build a workload from explicit lengths; tensors are drawn from ``rng``
     (or ``default_rng(seed)``), the page layout from ``default_rng(table_seed)``."""
     ctx_lens = np.asarray(ctx_lens, dtype=np.int32).reshape(-1)
@@ -193,7 +208,11 @@ def make_workload(*, seed: int, table_seed: Optional[int] = None, ctx_lens, q_le
                     ctx_lens=ctx_lens, q_lens=q_lens, query_start_loc=qsl,
                     block_table=bt, mm_ranges=mm, q=q_bits, k_new=k_new, v_new=v_new,
                     k_cache=k_cache, v_cache=v_cache, new_in_cache=new_in_cache,
-                    seed=seed, table_seed=table_seed)
+                    seed=seed, table_seed=table_seed,
+                    causal_per_seq=(None if causal_per_seq is None else
+                                    np.asarray(causal_per_seq, dtype=np.int32).reshape(S)),
+                    mm_clamp=bool(mm_clamp), chunk_size=int(chunk_size),
+                    chunk_lookback=int(chunk_lookback))
 
 
 # The five benchmark workloads.  Shapes follow the pages' own test shapes and
