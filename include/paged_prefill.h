@@ -147,6 +147,85 @@ int prefill_attention_tile_bounds(const int32_t* query_start_loc, const int32_t*
                                   const int32_t* mm_ranges, int32_t num_seqs, int32_t max_q_len,
                                   int32_t max_mm_ranges, int32_t* bounds_out, hipStream_t stream);
 
+/*
+ * prefill_attention_ex — prefill_attention with the mask variants and split-KV.  The first 24
+ * arguments are those of prefill_attention; prefill_attention(...) equals
+ * prefill_attention_ex(..., NULL, 1, 0, -1, 1, NULL, 0, stream).
+ *   causal_per_seq  device int32 [num_seqs] of 0/1, the causal flag of each sequence; NULL =
+ *                   `causal` for every sequence.  Contents are a precondition (0 or 1).
+ *   mm_clamp        1: a multimodal range admits keys j >= a - window_left only (the window-
+ *                   clamped prefix mask); 0: a query inside a range sees the whole range
+ *                   (vLLM PR #53147 report, "Implementation breakdown" item 1: the
+ *                   MM_PREFIX_CLAMP_SW switch).  Tile bounds stay tight in both modes.
+ *   chunk_size, chunk_lookback
+ *                   chunked local attention when chunk_size > 0 and chunk_lookback >= 0: the base
+ *                   window's left edge becomes (a / chunk_size - chunk_lookback) * chunk_size,
+ *                   the start of the chunk chunk_lookback chunks before the query's own; a
+ *                   multimodal range may still admit earlier keys, clamped by window_left when
+ *                   mm_clamp is 1 (vLLM PR #53147 report, "Key source snippets",
+ *                   compute_tile_loop_bounds, and "Review highlights").  chunk_size = 0 or
+ *                   chunk_lookback = -1: off.
+ *   kv_splits       split-KV (vLLM PR #53147 report, "Key source snippets": the segment
+ *                   arguments of the tile-bound helper): each Q tile's KV-tile range is cut into
+ *                   kv_splits contiguous segments handled by separate workgroups, whose partial
+ *                   results (unnormalised O, running max, running sum) are merged by the
+ *                   log-sum-exp rule in a second kernel on the same stream.  1 = no split,
+ *                   0 = automatic (prefill_attention_kv_splits tells the count), at most 64.
+ *   workspace, workspace_bytes
+ *                   device scratch owned by the caller, used when the split count is > 1; at
+ *                   least prefill_attention_workspace_size(num_heads, head_size, total_q_tokens,
+ *                   count) bytes, 256-byte aligned.  Unused (may be NULL) when the count is 1.
+ *                   Two calls in flight must not share a workspace.
+ * Errors: as prefill_attention, plus INVALID_ARG for mm_clamp not 0/1, chunk_size < 0,
+ * chunk_lookback < -1, kv_splits outside [0, 64], or a missing/short workspace.
+ */
+int prefill_attention_ex(const void* q, const void* k_new, const void* v_new,
+                         const void* k_cache, const void* v_cache,
+                         const int32_t* block_table, const int32_t* query_start_loc,
+                         const int32_t* ctx_lens,
+                         int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                         int32_t page_size, int32_t window_left, int32_t window_right,
+                         int32_t causal, const int32_t* mm_ranges, float scale, void* out,
+                         int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                         int32_t num_pages, int32_t max_pages_per_seq, int32_t max_mm_ranges,
+                         const int32_t* causal_per_seq, int32_t mm_clamp, int32_t chunk_size,
+                         int32_t chunk_lookback, int32_t kv_splits, void* workspace,
+                         uint64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * prefill_attention_kv_splits — the split count prefill_attention_ex uses for kv_splits
+ * (kv_splits itself when > 0; for 0, 1 when the batch has at least 512 Q-tile work items,
+ * else enough segments for about 512 workgroups, at most 16).  Host-only.  Returns the count
+ * (>= 1) or a negative error code (INVALID_ARG, UNSUPPORTED as for tile_config).
+ */
+int prefill_attention_kv_splits(int32_t head_size, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t num_seqs, int32_t max_q_len, int32_t kv_splits);
+
+/*
+ * prefill_attention_workspace_size — bytes of workspace prefill_attention_ex needs with
+ * `splits` segments (0 when splits <= 1, or for invalid sizes): fp32 partial outputs
+ * [splits][total_q_tokens][num_heads][head_size] then fp32 (max, sum) pairs
+ * [splits][total_q_tokens][num_heads].  Host-only.
+ */
+uint64_t prefill_attention_workspace_size(int32_t num_heads, int32_t head_size,
+                                          int32_t total_q_tokens, int32_t splits);
+
+/*
+ * prefill_attention_tile_bounds_ex — prefill_attention_tile_bounds under the mask variants of
+ * prefill_attention_ex (causal_per_seq, mm_clamp, chunk_size, chunk_lookback as there).  The
+ * chunked left edge is taken at the tile's lowest query row.  Split-KV does not change the
+ * bounds: a split only partitions [lo, hi).
+ */
+int prefill_attention_tile_bounds_ex(const int32_t* query_start_loc, const int32_t* ctx_lens,
+                                     int32_t num_heads, int32_t num_kv_heads,
+                                     int32_t head_size, int32_t window_left,
+                                     int32_t window_right, int32_t causal,
+                                     const int32_t* mm_ranges, int32_t num_seqs,
+                                     int32_t max_q_len, int32_t max_mm_ranges,
+                                     const int32_t* causal_per_seq, int32_t mm_clamp,
+                                     int32_t chunk_size, int32_t chunk_lookback,
+                                     int32_t* bounds_out, hipStream_t stream);
+
 /* prefill_attention_strerror — static description of an error code (never NULL). */
 const char* prefill_attention_strerror(int code);
 

@@ -13,9 +13,11 @@ from ._binding import (  # noqa: F401
     PrefillError,
     load_library,
     prefill_attention,
+    split_count,
     strerror,
     tile_bounds,
     tile_config,
     validate,
+    workspace_size,
 )
 from ._build import build, library_path  # noqa: F401

@@ -22,6 +22,7 @@ ERR_HIP = -3
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
 _F = ctypes.c_float
+_U64 = ctypes.c_uint64
 
 _SIGNATURES = {
     "prefill_attention": ([_P] * 8 + [_I] * 7 + [_P, _F, _P] + [_I] * 6 + [_P], _I),
@@ -29,6 +30,12 @@ _SIGNATURES = {
     "prefill_attention_tile_config": ([_I, _I, _I, _P, _P], _I),
     "prefill_attention_tile_bounds": ([_P, _P] + [_I] * 6 + [_P] + [_I] * 3 + [_P, _P], _I),
     "prefill_attention_strerror": ([_I], ctypes.c_char_p),
+    "prefill_attention_ex": ([_P] * 8 + [_I] * 7 + [_P, _F, _P] + [_I] * 6
+                             + [_P, _I, _I, _I, _I, _P, _U64, _P], _I),
+    "prefill_attention_kv_splits": ([_I] * 6, _I),
+    "prefill_attention_workspace_size": ([_I] * 4, _U64),
+    "prefill_attention_tile_bounds_ex": ([_P, _P] + [_I] * 6 + [_P] + [_I] * 3
+                                         + [_P, _I, _I, _I, _P, _P], _I),
 }
 
 _lib = None
@@ -95,17 +102,37 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def split_count(head_size: int, num_heads: int, num_kv_heads: int, num_seqs: int,
+                max_q_len: int, requested: int = 0) -> int:
+    """The split-KV segment count the library uses for ``requested`` (0 = automatic)."""
+    rc = load_library().prefill_attention_kv_splits(head_size, num_heads, num_kv_heads,
+                                                    num_seqs, max_q_len, requested)
+    if rc < 0:
+        raise PrefillError(rc, "prefill_attention_kv_splits")
+    return rc
+
+
+def workspace_size(num_heads: int, head_size: int, total_q_tokens: int, splits: int) -> int:
+    return int(load_library().prefill_attention_workspace_size(num_heads, head_size,
+                                                               total_q_tokens, splits))
+
+
 def prefill_attention(q, k_new, v_new, k_cache, v_cache, block_table, query_start_loc,
                       ctx_lens, num_heads: int, num_kv_heads: int, head_size: int,
                       page_size: int, window_left: int, window_right: int, causal: bool,
                       mm_ranges, scale: float, out=None, *, max_q_len: Optional[int] = None,
-                      stream=None):
+                      stream=None, causal_per_seq=None, mm_clamp: bool = True,
+                      chunk_size: int = 0, chunk_lookback: int = -1, kv_splits: int = 1,
+                      workspace=None):
     """Paged-KV prefill attention; returns ``out`` (bf16 [T, H, d]).
 
     ``k_new = v_new = None`` selects the cache-sourced mode.  ``max_q_len``
     (the largest new-token count of a sequence) should be passed by callers
     that know it; when omitted it is read back from ``query_start_loc``,
-    which synchronises the stream.
+    which synchronises the stream.  The keyword-only mask variants and
+    ``kv_splits`` select ``prefill_attention_ex``; with more than one split a
+    workspace is taken from ``workspace`` (a uint8 device tensor) or
+    allocated through torch.
     """
     import torch
     H, Hkv, d, P = int(num_heads), int(num_kv_heads), int(head_size), int(page_size)
@@ -138,19 +165,40 @@ def prefill_attention(q, k_new, v_new, k_cache, v_cache, block_table, query_star
     _check(out, "out", torch.bfloat16, (T, H, d))
     if max_q_len is None:
         max_q_len = int((query_start_loc[1:] - query_start_loc[:-1]).max().item()) if S else 0
-    rc = load_library().prefill_attention(
-        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-        _ptr(query_start_loc), _ptr(ctx_lens), H, Hkv, d, P, int(window_left),
-        int(window_right), int(bool(causal)), _ptr(mm_ranges), float(scale), _ptr(out), S, T,
-        int(max_q_len), num_pages, int(block_table.shape[1]), R, _stream(stream))
+    base = (_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            _ptr(query_start_loc), _ptr(ctx_lens), H, Hkv, d, P, int(window_left),
+            int(window_right), int(bool(causal)), _ptr(mm_ranges), float(scale), _ptr(out), S,
+            T, int(max_q_len), num_pages, int(block_table.shape[1]), R)
+    plain = (causal_per_seq is None and mm_clamp and chunk_size == 0 and chunk_lookback == -1
+             and kv_splits == 1)
+    if plain:
+        rc = load_library().prefill_attention(*base, _stream(stream))
+        if rc != OK:
+            raise PrefillError(rc, "prefill_attention")
+        return out
+    if causal_per_seq is not None:
+        _check(causal_per_seq, "causal_per_seq", torch.int32, (S,))
+    splits = split_count(d, H, Hkv, S, int(max_q_len), int(kv_splits))
+    need = workspace_size(H, d, T, splits)
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _check(workspace, "workspace", torch.uint8)
+        if workspace.numel() < need:
+            raise ValueError("workspace needs %d bytes" % need)
+    ws_bytes = 0 if workspace is None else int(workspace.numel())
+    rc = load_library().prefill_attention_ex(
+        *base, _ptr(causal_per_seq), int(bool(mm_clamp)), int(chunk_size), int(chunk_lookback),
+        int(kv_splits), _ptr(workspace), ws_bytes, _stream(stream))
     if rc != OK:
-        raise PrefillError(rc, "prefill_attention")
+        raise PrefillError(rc, "prefill_attention_ex")
     return out
 
 
 def tile_bounds(query_start_loc, ctx_lens, num_heads: int, num_kv_heads: int, head_size: int,
                 window_left: int, window_right: int, causal: bool, mm_ranges, max_q_len: int,
-                stream=None):
+                stream=None, *, causal_per_seq=None, mm_clamp: bool = True,
+                chunk_size: int = 0, chunk_lookback: int = -1):
     """int32 [S, cdiv(max_q_len, block_q), 2] of (lo, hi) KV-tile loop ranges, on device."""
     import torch
     S = int(ctx_lens.shape[0])
@@ -165,12 +213,15 @@ def tile_bounds(query_start_loc, ctx_lens, num_heads: int, num_kv_heads: int, he
     bq, _ = tile_config(head_size, num_heads, num_kv_heads)
     nt = -(-int(max_q_len) // bq)
     out = torch.empty((S, nt, 2), dtype=torch.int32, device=ctx_lens.device)
-    rc = load_library().prefill_attention_tile_bounds(
+    if causal_per_seq is not None:
+        _check(causal_per_seq, "causal_per_seq", torch.int32, (S,))
+    rc = load_library().prefill_attention_tile_bounds_ex(
         _ptr(query_start_loc), _ptr(ctx_lens), int(num_heads), int(num_kv_heads),
         int(head_size), int(window_left), int(window_right), int(bool(causal)), _ptr(mm_ranges),
-        S, int(max_q_len), R, _ptr(out), _stream(stream))
+        S, int(max_q_len), R, _ptr(causal_per_seq), int(bool(mm_clamp)), int(chunk_size),
+        int(chunk_lookback), _ptr(out), _stream(stream))
     if rc != OK:
-        raise PrefillError(rc, "prefill_attention_tile_bounds")
+        raise PrefillError(rc, "prefill_attention_tile_bounds_ex")
     return out
 
 

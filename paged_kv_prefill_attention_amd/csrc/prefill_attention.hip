@@ -98,32 +98,66 @@ struct KernelArgs {
   int32_t max_mm_ranges;
   int32_t cache_only;      // 1: every position comes from the cache
   int32_t num_q_tiles;     // cdiv(max_q_len, block_q)
+  const int32_t* causal_per_seq;  // [num_seqs] or null (then `causal`)
+  int32_t mm_clamp;
+  int32_t chunk_size;
+  int32_t chunk_lookback;
+  int32_t kv_splits;       // KV segments per Q tile (1: no split)
+  int32_t total_q_tokens;
+  float* part_o;           // [kv_splits][T][H][d] unnormalised partial O (kv_splits > 1)
+  float2* part_ml;         // [kv_splits][T][H] (m, l) of each partial, log2 units
 };
 
 // ---------------------------------------------------------------------------
-// Tile bound calculator.  Query rows of tile t are [t*block_q, min(..., n)-1];
-// the base window runs from a_lo - window_left (key 0 without a left window)
-// to a_hi (causal), a_hi + window_right, or the last key; every valid range
-// [st, en] (st < en) overlapping [a_lo, a_hi] may lower the left edge to
-// max(st, a_lo - window_left) and raise the right edge to en; the result is
-// clamped to [0, L-1] and converted to KV tiles of `block_n` keys.
+// Mask of one sequence.  A key j < L is allowed for the query at absolute
+// position a when the base window admits it:
+//   causal => j <= a;  left edge: the chunk start (a / chunk_size -
+//   chunk_lookback) * chunk_size in chunked local attention, else a -
+//   window_left when window_left >= 0;  !causal and window_right >= 0 =>
+//   j <= a + window_right;
+// or when a valid multimodal range [st, en] (st < en) holds both a and j and,
+// with the window clamp on, j >= a - window_left.  (vLLM PR #53147 report,
+// "Key source snippets", compute_tile_loop_bounds; "Review highlights".)
 // ---------------------------------------------------------------------------
+struct MaskSpec {
+  int causal;
+  int wl, wr;
+  int chunk_size, chunk_lookback;  // chunked when chunk_size > 0 and chunk_lookback >= 0
+  int mm_clamp;                    // 1: a range is clamped on the left by window_left
+};
+
+__device__ __forceinline__ int base_left(int a, const MaskSpec& m) {
+  if (m.chunk_size > 0 && m.chunk_lookback >= 0)
+    return (a / m.chunk_size - m.chunk_lookback) * m.chunk_size;
+  return m.wl >= 0 ? a - m.wl : 0;
+}
+__device__ __forceinline__ int range_left(int st, int a, const MaskSpec& m) {
+  return (m.mm_clamp && m.wl >= 0) ? max(st, a - m.wl) : st;
+}
+
+// Tile bound calculator.  Query rows of tile t are [t*block_q, min(..., n)-1];
+// the base window runs from base_left(a_lo) to a_hi (causal), a_hi +
+// window_right, or the last key; every valid range [st, en] overlapping
+// [a_lo, a_hi] may lower the left edge to range_left(st, a_lo) and raise the
+// right edge to en; the result is clamped to [0, L-1] and converted to KV
+// tiles of `block_n` keys.  Left edges are taken at the tile's lowest row,
+// where they are smallest.
 __device__ __forceinline__ int2 kv_tile_range(int c, int n, int t, int block_q, int block_n,
-                                              int causal, int wl, int wr,
-                                              const int32_t* ranges, int num_ranges) {
+                                              const MaskSpec& m, const int32_t* ranges,
+                                              int num_ranges) {
   const int i_lo = t * block_q;
   if (i_lo >= n) return make_int2(0, 0);
   const int i_hi = min(i_lo + block_q - 1, n - 1);
   const int L = c + n;
   const int a_lo = c + i_lo;
   const int a_hi = c + i_hi;
-  int first = wl >= 0 ? a_lo - wl : 0;
-  int last = causal ? a_hi : (wr >= 0 ? a_hi + min(wr, L) : L - 1);
+  int first = base_left(a_lo, m);
+  int last = m.causal ? a_hi : (m.wr >= 0 ? a_hi + min(m.wr, L) : L - 1);
   for (int r = 0; r < num_ranges; ++r) {
     const int st = ranges[2 * r];
     const int en = ranges[2 * r + 1];
     if (st < en && st <= a_hi && en >= a_lo) {
-      first = min(first, wl >= 0 ? max(st, a_lo - wl) : st);
+      first = min(first, range_left(st, a_lo, m));
       last = max(last, en);
     }
   }
@@ -135,16 +169,16 @@ __device__ __forceinline__ int2 kv_tile_range(int c, int n, int t, int block_q, 
 // Allowed keys of the query at absolute position a: one interval [lo, hi].
 // The base window always contains j = a, and every multimodal range that
 // admits the query contains a as well, so their union is a single interval.
-__device__ __forceinline__ void row_interval(int a, int L, int causal, int wl, int wr,
+__device__ __forceinline__ void row_interval(int a, int L, const MaskSpec& m,
                                              const int32_t* ranges, int num_ranges,
                                              int& lo, int& hi) {
-  lo = wl >= 0 ? a - wl : 0;
-  hi = causal ? a : (wr >= 0 ? a + min(wr, L) : L - 1);
+  lo = base_left(a, m);
+  hi = m.causal ? a : (m.wr >= 0 ? a + min(m.wr, L) : L - 1);
   for (int r = 0; r < num_ranges; ++r) {
     const int st = ranges[2 * r];
     const int en = ranges[2 * r + 1];
     if (st < en && st <= a && a <= en) {
-      lo = min(lo, wl >= 0 ? max(st, a - wl) : st);
+      lo = min(lo, range_left(st, a, m));
       hi = max(hi, en);
     }
   }
@@ -384,7 +418,11 @@ void prefill_attention_kernel(const KernelArgs p) {
   __shared__ int sched_seq[kSortMaxSeqs];
   __shared__ int sched_ntiles[kSortMaxSeqs];
   const int tid = threadIdx.x;
-  const WorkItem wi = decode_work(p, blockIdx.x, tid, C::THREADS, sched_seq, sched_ntiles);
+  // Split-KV: the kv_splits segments of one work item take consecutive slots
+  // of the same XCD.
+  const int split = (int)((blockIdx.x / kNumXcd) % p.kv_splits);
+  const int bitem = (int)((blockIdx.x / kNumXcd) / p.kv_splits) * kNumXcd + blockIdx.x % kNumXcd;
+  const WorkItem wi = decode_work(p, bitem, tid, C::THREADS, sched_seq, sched_ntiles);
   if (!wi.valid) return;  // padding slot
   const int s = wi.s;
   const int g = wi.g;
@@ -399,8 +437,18 @@ void prefill_attention_kernel(const KernelArgs p) {
   const int32_t* ranges = R > 0 ? p.mm_ranges + (int64_t)s * R * 2 : nullptr;
   const int32_t* bt = p.block_table + (int64_t)s * p.max_pages_per_seq;
 
-  const int2 tb = kv_tile_range(c, n, t, p.block_q, BN, p.causal, p.window_left,
-                                p.window_right, ranges, R);
+  const MaskSpec mspec{p.causal_per_seq != nullptr ? p.causal_per_seq[s] : p.causal,
+                       p.window_left, p.window_right, p.chunk_size, p.chunk_lookback,
+                       p.mm_clamp};
+  int2 tb = kv_tile_range(c, n, t, p.block_q, BN, mspec, ranges, R);
+  if (p.kv_splits > 1) {  // this item's segment of the tile range (possibly empty)
+    const int per = (tb.y - tb.x + p.kv_splits - 1) / p.kv_splits;
+    const int x0 = min(tb.x + split * per, tb.y);
+    tb = make_int2(x0, min(x0 + per, tb.y));
+  }
+  // wave-uniform: keeps the loop bounds and copy bases in scalar registers
+  tb.x = __builtin_amdgcn_readfirstlane(tb.x);
+  tb.y = __builtin_amdgcn_readfirstlane(tb.y);
 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -422,8 +470,7 @@ void prefill_attention_kernel(const KernelArgs p) {
     lo_a[rb] = 1;
     hi_a[rb] = 0;
     if (valid[rb]) {
-      row_interval(c + tok[rb], L, p.causal, p.window_left, p.window_right, ranges, R,
-                   lo_a[rb], hi_a[rb]);
+      row_interval(c + tok[rb], L, mspec, ranges, R, lo_a[rb], hi_a[rb]);
       lo_max = max(lo_max, lo_a[rb]);
       hi_min = min(hi_min, hi_a[rb]);
       lo_min = min(lo_min, lo_a[rb]);
@@ -850,6 +897,30 @@ void prefill_attention_kernel(const KernelArgs p) {
     pv(it % NSTAGE, pf);
   }
 
+  // ---- split-KV epilogue: the segment's unnormalised O with its reference max
+  // m and sum l (log2 units), merged by merge_splits_kernel.
+  if (p.kv_splits > 1) {
+    const int64_t rows = (int64_t)p.total_q_tokens * p.num_heads;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float l_tot = pair_sum(l_run[rb]);
+      if (!valid[rb]) continue;
+      const int64_t ri = (int64_t)split * rows + (int64_t)(q0 + tok[rb]) * p.num_heads + head[rb];
+      if (half == 0) p.part_ml[ri] = make_float2(m_run[rb], l_tot);
+      if (l_tot > 0.f) {
+        float* orow = p.part_o + ri * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int b4 = 0; b4 < 4; ++b4) {
+            const f32x16& o = oacc[rb][db];
+            *(f32x4*)(orow + db * 32 + 8 * b4 + 4 * half) =
+                f32x4{o[4 * b4], o[4 * b4 + 1], o[4 * b4 + 2], o[4 * b4 + 3]};
+          }
+      }
+    }
+    return;
+  }
   // ---- epilogue: O / l -> bf16; lane holds dims 32db + 8(r/4) + 4half + r%4
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -873,19 +944,57 @@ void prefill_attention_kernel(const KernelArgs p) {
 
 // One lane per (sequence, Q tile): the loop range the attention kernel uses.
 __global__ void tile_bounds_kernel(const int32_t* qsl, const int32_t* ctx_lens,
-                                   const int32_t* mm_ranges, int num_seqs, int num_q_tiles,
-                                   int block_q, int block_n, int causal, int wl, int wr,
-                                   int num_ranges, int32_t* out) {
+                                   const int32_t* mm_ranges, const int32_t* causal_per_seq,
+                                   int num_seqs, int num_q_tiles, int block_q, int block_n,
+                                   MaskSpec m, int num_ranges, int32_t* out) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)num_seqs * num_q_tiles) return;
   const int s = (int)(idx / num_q_tiles);
   const int t = (int)(idx - (int64_t)s * num_q_tiles);
   const int n = qsl[s + 1] - qsl[s];
   const int32_t* ranges = num_ranges > 0 ? mm_ranges + (int64_t)s * num_ranges * 2 : nullptr;
-  const int2 r = kv_tile_range(ctx_lens[s], n, t, block_q, block_n, causal, wl, wr, ranges,
-                               num_ranges);
+  if (causal_per_seq != nullptr) m.causal = causal_per_seq[s];
+  const int2 r = kv_tile_range(ctx_lens[s], n, t, block_q, block_n, m, ranges, num_ranges);
   out[2 * idx] = r.x;
   out[2 * idx + 1] = r.y;
+}
+
+// Split-KV merge (log-sum-exp rule): for each (token, head) row,
+//   out = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k,  M = max over segments
+// with l_k > 0.  One thread per 8 output dims.
+template <int D>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void merge_splits_kernel(const float* part_o, const float2* part_ml, uint16_t* out,
+                         int64_t rows, int splits) {
+  constexpr int TPR = D / 8;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid / TPR;
+  const int sub = (int)(gid - row * TPR);
+  if (row >= rows) return;
+  float M = -INFINITY;
+  for (int k = 0; k < splits; ++k) {
+    const float2 ml = part_ml[k * rows + row];
+    if (ml.y > 0.f) M = fmaxf(M, ml.x);
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  for (int k = 0; k < splits; ++k) {
+    const float2 ml = part_ml[k * rows + row];
+    if (!(ml.y > 0.f)) continue;
+    const float w = exp2f(ml.x - M);
+    den += w * ml.y;
+    const f32x4* src = (const f32x4*)(part_o + (k * rows + row) * D + sub * 8);
+    const f32x4 a = src[0], b = src[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += w * a[e];
+      acc[4 + e] += w * b[e];
+    }
+  }
+  const float inv = 1.f / den;
+  const f32x8 v = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv,
+                   acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+  *(u32x4*)(out + row * D + sub * 8) = __builtin_bit_cast(u32x4, __builtin_convertvector(v, bf16x8));
 }
 
 // ---------------------------------------------------------------------------
@@ -930,6 +1039,18 @@ int choose_tiles(int head_size, int num_heads, int num_kv_heads, TileChoice* tc)
   return PAGED_PREFILL_OK;
 }
 
+struct Options {
+  const int32_t* causal_per_seq = nullptr;
+  int32_t mm_clamp = 1;
+  int32_t chunk_size = 0;
+  int32_t chunk_lookback = -1;
+  int32_t kv_splits = 1;
+  void* workspace = nullptr;
+  uint64_t workspace_bytes = 0;
+};
+
+constexpr int kMaxSplits = 64;
+
 int validate(const void* q, const void* k_new, const void* v_new, const void* k_cache,
              const void* v_cache, const int32_t* block_table, const int32_t* qsl,
              const int32_t* ctx_lens, int32_t num_heads, int32_t num_kv_heads,
@@ -960,6 +1081,13 @@ int validate(const void* q, const void* k_new, const void* v_new, const void* k_
   return PAGED_PREFILL_OK;
 }
 
+int validate_mask_options(const Options& o) {
+  if (o.mm_clamp != 0 && o.mm_clamp != 1) return PAGED_PREFILL_ERR_INVALID_ARG;
+  if (o.chunk_size < 0 || o.chunk_lookback < -1) return PAGED_PREFILL_ERR_INVALID_ARG;
+  if (o.chunk_size > kMaxTokens) return PAGED_PREFILL_ERR_INVALID_ARG;
+  return PAGED_PREFILL_OK;
+}
+
 void page_magic(int page_size, uint32_t* magic, int* shift) {
   int l = 0;
   while ((1 << l) < page_size) ++l;  // l = ceil(log2(page_size))
@@ -968,12 +1096,178 @@ void page_magic(int page_size, uint32_t* magic, int* shift) {
   *shift = 24 + l;
 }
 
+// Workgroups per split before the split factor: 8 XCDs x slots per XCD.
+int64_t item_slots(int num_seqs, int num_kv_heads, int64_t num_q_tiles, int head_blocks) {
+  // slots per XCD: every group an XCD can own, each with up to num_q_tiles tiles
+  const int64_t groups_per_xcd = num_seqs <= kSortMaxSeqs
+      ? (int64_t)num_seqs * ((num_kv_heads + kNumXcd - 1) / kNumXcd)
+      : ((int64_t)num_seqs * num_kv_heads + kNumXcd - 1) / kNumXcd;
+  return kNumXcd * groups_per_xcd * num_q_tiles * head_blocks;
+}
+
+// Split count for kv_splits (0 = automatic): split only when the batch has
+// fewer Q-tile work items than twice the 256 CUs, to about 512 workgroups.
+int resolve_splits(int kv_splits, int num_seqs, int num_kv_heads, int head_blocks,
+                   int64_t num_q_tiles) {
+  if (kv_splits > 0) return kv_splits;
+  const int64_t items = (int64_t)num_seqs * num_kv_heads * head_blocks * num_q_tiles;
+  if (items >= 512 || items <= 0) return 1;
+  return (int)std::min<int64_t>(16, (512 + items - 1) / items);
+}
+
+uint64_t workspace_bytes_for(int num_heads, int head_size, int total_q_tokens, int splits) {
+  if (splits <= 1) return 0;
+  const uint64_t rows = (uint64_t)splits * (uint64_t)total_q_tokens * (uint64_t)num_heads;
+  const uint64_t o_bytes = (rows * head_size * sizeof(float) + 255) & ~(uint64_t)255;
+  return o_bytes + rows * 2 * sizeof(float);
+}
+
 template <int D>
 hipError_t launch(const KernelArgs& a, uint32_t grid, hipStream_t stream) {
   using C = typename ShapeFor<D>::T;
   void* args[] = {(void*)&a};
-  return hipLaunchKernel((const void*)&prefill_attention_kernel<C>, dim3(grid),
-                         dim3(C::THREADS), args, 0, stream);
+  hipError_t err = hipLaunchKernel((const void*)&prefill_attention_kernel<C>, dim3(grid),
+                                   dim3(C::THREADS), args, 0, stream);
+  if (err != hipSuccess || a.kv_splits <= 1) return err;
+  const int64_t rows = (int64_t)a.total_q_tokens * a.num_heads;
+  const int64_t threads = rows * (D / 8);
+  const float* po = a.part_o;
+  const float2* pml = a.part_ml;
+  uint16_t* out = a.out;
+  int64_t r = rows;
+  int k = a.kv_splits;
+  void* margs[] = {(void*)&po, (void*)&pml, (void*)&out, (void*)&r, (void*)&k};
+  return hipLaunchKernel((const void*)&merge_splits_kernel<D>,
+                         dim3((uint32_t)((threads + 255) / 256)), dim3(256), margs, 0, stream);
+}
+
+int run(const void* q, const void* k_new, const void* v_new, const void* k_cache,
+        const void* v_cache, const int32_t* block_table, const int32_t* query_start_loc,
+        const int32_t* ctx_lens, int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+        int32_t page_size, int32_t window_left, int32_t window_right, int32_t causal,
+        const int32_t* mm_ranges, float scale, void* out, int32_t num_seqs,
+        int32_t total_q_tokens, int32_t max_q_len, int32_t num_pages,
+        int32_t max_pages_per_seq, int32_t max_mm_ranges, const Options& o,
+        hipStream_t stream) {
+  int rc = validate(q, k_new, v_new, k_cache, v_cache, block_table, query_start_loc, ctx_lens,
+                    num_heads, num_kv_heads, head_size, page_size, window_left, window_right,
+                    causal, mm_ranges, scale, out, num_seqs, total_q_tokens, max_q_len,
+                    num_pages, max_pages_per_seq, max_mm_ranges);
+  if (rc != PAGED_PREFILL_OK) return rc;
+  rc = validate_mask_options(o);
+  if (rc != PAGED_PREFILL_OK) return rc;
+  if (o.kv_splits < 0 || o.kv_splits > kMaxSplits) return PAGED_PREFILL_ERR_INVALID_ARG;
+  if (num_seqs == 0 || total_q_tokens == 0 || max_q_len == 0) return PAGED_PREFILL_OK;
+  TileChoice tc;
+  rc = choose_tiles(head_size, num_heads, num_kv_heads, &tc);
+  if (rc != PAGED_PREFILL_OK) return rc;
+
+  KernelArgs a;
+  a.q = (const uint16_t*)q;
+  a.k_new = (const uint16_t*)k_new;
+  a.v_new = (const uint16_t*)v_new;
+  a.k_cache = (const uint16_t*)k_cache;
+  a.v_cache = (const uint16_t*)v_cache;
+  a.block_table = block_table;
+  a.qsl = query_start_loc;
+  a.ctx_lens = ctx_lens;
+  a.mm_ranges = max_mm_ranges > 0 ? mm_ranges : nullptr;
+  a.out = (uint16_t*)out;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_heads / num_kv_heads;
+  a.heads_per_tile = tc.heads_per_tile;
+  a.head_blocks = a.group / tc.heads_per_tile;
+  a.block_q = tc.block_q;
+  a.page_size = page_size;
+  page_magic(page_size, &a.page_magic, &a.page_shift);
+  a.window_left = window_left;
+  a.window_right = window_right;
+  a.causal = causal;
+  a.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
+  a.num_seqs = num_seqs;
+  a.max_pages_per_seq = max_pages_per_seq;
+  a.max_mm_ranges = max_mm_ranges;
+  a.cache_only = k_new == nullptr ? 1 : 0;
+  a.causal_per_seq = o.causal_per_seq;
+  a.mm_clamp = o.mm_clamp;
+  a.chunk_size = o.chunk_size;
+  a.chunk_lookback = o.chunk_lookback;
+  a.total_q_tokens = total_q_tokens;
+
+  const int64_t num_q_tiles = ((int64_t)max_q_len + tc.block_q - 1) / tc.block_q;
+  a.num_q_tiles = (int32_t)num_q_tiles;
+  const int splits = resolve_splits(o.kv_splits, num_seqs, num_kv_heads, a.head_blocks,
+                                    num_q_tiles);
+  a.kv_splits = splits;
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  if (splits > 1) {
+    const uint64_t need = workspace_bytes_for(num_heads, head_size, total_q_tokens, splits);
+    if (o.workspace == nullptr || o.workspace_bytes < need) return PAGED_PREFILL_ERR_INVALID_ARG;
+    const uint64_t rows = (uint64_t)splits * total_q_tokens * num_heads;
+    const uint64_t o_bytes = (rows * head_size * sizeof(float) + 255) & ~(uint64_t)255;
+    a.part_o = (float*)o.workspace;
+    a.part_ml = (float2*)((char*)o.workspace + o_bytes);
+  }
+  const int64_t grid = item_slots(num_seqs, num_kv_heads, num_q_tiles, a.head_blocks) * splits;
+  if (grid > 0x7fffffff) return PAGED_PREFILL_ERR_UNSUPPORTED;
+  hipError_t err;
+  switch (head_size) {
+    case 64: err = launch<64>(a, (uint32_t)grid, stream); break;
+    case 128: err = launch<128>(a, (uint32_t)grid, stream); break;
+    default: err = launch<256>(a, (uint32_t)grid, stream); break;
+  }
+  return err == hipSuccess ? PAGED_PREFILL_OK : PAGED_PREFILL_ERR_HIP;
+}
+
+int run_tile_bounds(const int32_t* query_start_loc, const int32_t* ctx_lens, int32_t num_heads,
+                    int32_t num_kv_heads, int32_t head_size, int32_t window_left,
+                    int32_t window_right, int32_t causal, const int32_t* mm_ranges,
+                    int32_t num_seqs, int32_t max_q_len, int32_t max_mm_ranges,
+                    const Options& o, int32_t* bounds_out, hipStream_t stream) {
+  TileChoice tc;
+  int rc = choose_tiles(head_size, num_heads, num_kv_heads, &tc);
+  if (rc != PAGED_PREFILL_OK) return rc;
+  if (num_seqs < 0 || max_q_len < 0 || max_q_len > kMaxTokens || window_left < -1 ||
+      window_right < -1 || (causal != 0 && causal != 1) || max_mm_ranges < 0 ||
+      max_mm_ranges > kMaxMmRanges || (max_mm_ranges > 0 && mm_ranges == nullptr))
+    return PAGED_PREFILL_ERR_INVALID_ARG;
+  rc = validate_mask_options(o);
+  if (rc != PAGED_PREFILL_OK) return rc;
+  const int64_t num_q_tiles = ((int64_t)max_q_len + tc.block_q - 1) / tc.block_q;
+  const int64_t total = num_q_tiles * num_seqs;
+  if (total == 0) return PAGED_PREFILL_OK;
+  if (query_start_loc == nullptr || ctx_lens == nullptr || bounds_out == nullptr)
+    return PAGED_PREFILL_ERR_INVALID_ARG;
+  if (total > 0x7fffffffLL) return PAGED_PREFILL_ERR_UNSUPPORTED;
+  const int threads = 256;
+  const uint32_t blocks = (uint32_t)((total + threads - 1) / threads);
+  const int32_t* mm = max_mm_ranges > 0 ? mm_ranges : nullptr;
+  const int32_t* cps = o.causal_per_seq;
+  int ns = num_seqs, nt = (int)num_q_tiles, bq = tc.block_q, bn = tc.block_n;
+  MaskSpec m{causal, window_left, window_right, o.chunk_size, o.chunk_lookback, o.mm_clamp};
+  int nr = max_mm_ranges;
+  void* args[] = {(void*)&query_start_loc, (void*)&ctx_lens, (void*)&mm, (void*)&cps,
+                  (void*)&ns, (void*)&nt, (void*)&bq, (void*)&bn, (void*)&m, (void*)&nr,
+                  (void*)&bounds_out};
+  const hipError_t err = hipLaunchKernel((const void*)&tile_bounds_kernel, dim3(blocks),
+                                         dim3(threads), args, 0, stream);
+  return err == hipSuccess ? PAGED_PREFILL_OK : PAGED_PREFILL_ERR_HIP;
+}
+
+Options make_options(const int32_t* causal_per_seq, int32_t mm_clamp, int32_t chunk_size,
+                     int32_t chunk_lookback, int32_t kv_splits, void* workspace,
+                     uint64_t workspace_bytes) {
+  Options o;
+  o.causal_per_seq = causal_per_seq;
+  o.mm_clamp = mm_clamp;
+  o.chunk_size = chunk_size;
+  o.chunk_lookback = chunk_lookback;
+  o.kv_splits = kv_splits;
+  o.workspace = workspace;
+  o.workspace_bytes = workspace_bytes;
+  return o;
 }
 
 }  // namespace
@@ -1026,59 +1320,48 @@ int prefill_attention(const void* q, const void* k_new, const void* v_new,
                       int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
                       int32_t num_pages, int32_t max_pages_per_seq, int32_t max_mm_ranges,
                       hipStream_t stream) {
-  int rc = validate(q, k_new, v_new, k_cache, v_cache, block_table, query_start_loc, ctx_lens,
-                    num_heads, num_kv_heads, head_size, page_size, window_left, window_right,
-                    causal, mm_ranges, scale, out, num_seqs, total_q_tokens, max_q_len,
-                    num_pages, max_pages_per_seq, max_mm_ranges);
-  if (rc != PAGED_PREFILL_OK) return rc;
-  if (num_seqs == 0 || total_q_tokens == 0 || max_q_len == 0) return PAGED_PREFILL_OK;
+  return run(q, k_new, v_new, k_cache, v_cache, block_table, query_start_loc, ctx_lens,
+             num_heads, num_kv_heads, head_size, page_size, window_left, window_right, causal,
+             mm_ranges, scale, out, num_seqs, total_q_tokens, max_q_len, num_pages,
+             max_pages_per_seq, max_mm_ranges, Options(), stream);
+}
+
+int prefill_attention_ex(const void* q, const void* k_new, const void* v_new,
+                         const void* k_cache, const void* v_cache, const int32_t* block_table,
+                         const int32_t* query_start_loc, const int32_t* ctx_lens,
+                         int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                         int32_t page_size, int32_t window_left, int32_t window_right,
+                         int32_t causal, const int32_t* mm_ranges, float scale, void* out,
+                         int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                         int32_t num_pages, int32_t max_pages_per_seq, int32_t max_mm_ranges,
+                         const int32_t* causal_per_seq, int32_t mm_clamp, int32_t chunk_size,
+                         int32_t chunk_lookback, int32_t kv_splits, void* workspace,
+                         uint64_t workspace_bytes, hipStream_t stream) {
+  return run(q, k_new, v_new, k_cache, v_cache, block_table, query_start_loc, ctx_lens,
+             num_heads, num_kv_heads, head_size, page_size, window_left, window_right, causal,
+             mm_ranges, scale, out, num_seqs, total_q_tokens, max_q_len, num_pages,
+             max_pages_per_seq, max_mm_ranges,
+             make_options(causal_per_seq, mm_clamp, chunk_size, chunk_lookback, kv_splits,
+                          workspace, workspace_bytes),
+             stream);
+}
+
+int prefill_attention_kv_splits(int32_t head_size, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t num_seqs, int32_t max_q_len, int32_t kv_splits) {
+  if (kv_splits < 0 || kv_splits > kMaxSplits || num_seqs < 0 || max_q_len < 0)
+    return PAGED_PREFILL_ERR_INVALID_ARG;
   TileChoice tc;
-  rc = choose_tiles(head_size, num_heads, num_kv_heads, &tc);
+  const int rc = choose_tiles(head_size, num_heads, num_kv_heads, &tc);
   if (rc != PAGED_PREFILL_OK) return rc;
-
-  KernelArgs a;
-  a.q = (const uint16_t*)q;
-  a.k_new = (const uint16_t*)k_new;
-  a.v_new = (const uint16_t*)v_new;
-  a.k_cache = (const uint16_t*)k_cache;
-  a.v_cache = (const uint16_t*)v_cache;
-  a.block_table = block_table;
-  a.qsl = query_start_loc;
-  a.ctx_lens = ctx_lens;
-  a.mm_ranges = max_mm_ranges > 0 ? mm_ranges : nullptr;
-  a.out = (uint16_t*)out;
-  a.num_heads = num_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.group = num_heads / num_kv_heads;
-  a.heads_per_tile = tc.heads_per_tile;
-  a.head_blocks = a.group / tc.heads_per_tile;
-  a.block_q = tc.block_q;
-  a.page_size = page_size;
-  page_magic(page_size, &a.page_magic, &a.page_shift);
-  a.window_left = window_left;
-  a.window_right = window_right;
-  a.causal = causal;
-  a.scale_log2 = scale * 1.4426950408889634f;  // log2(e)
-  a.num_seqs = num_seqs;
-  a.max_pages_per_seq = max_pages_per_seq;
-  a.max_mm_ranges = max_mm_ranges;
-  a.cache_only = k_new == nullptr ? 1 : 0;
-
   const int64_t num_q_tiles = ((int64_t)max_q_len + tc.block_q - 1) / tc.block_q;
-  a.num_q_tiles = (int32_t)num_q_tiles;
-  // slots per XCD: every group an XCD can own, each with up to num_q_tiles tiles
-  const int64_t groups_per_xcd = num_seqs <= kSortMaxSeqs
-      ? (int64_t)num_seqs * ((num_kv_heads + kNumXcd - 1) / kNumXcd)
-      : ((int64_t)num_seqs * num_kv_heads + kNumXcd - 1) / kNumXcd;
-  const int64_t grid = kNumXcd * groups_per_xcd * num_q_tiles * a.head_blocks;
-  if (grid > 0x7fffffff) return PAGED_PREFILL_ERR_UNSUPPORTED;
-  hipError_t err;
-  switch (head_size) {
-    case 64: err = launch<64>(a, (uint32_t)grid, stream); break;
-    case 128: err = launch<128>(a, (uint32_t)grid, stream); break;
-    default: err = launch<256>(a, (uint32_t)grid, stream); break;
-  }
-  return err == hipSuccess ? PAGED_PREFILL_OK : PAGED_PREFILL_ERR_HIP;
+  return resolve_splits(kv_splits, num_seqs, num_kv_heads,
+                        num_heads / num_kv_heads / tc.heads_per_tile, num_q_tiles);
+}
+
+uint64_t prefill_attention_workspace_size(int32_t num_heads, int32_t head_size,
+                                          int32_t total_q_tokens, int32_t splits) {
+  if (num_heads <= 0 || head_size <= 0 || total_q_tokens < 0 || splits < 0) return 0;
+  return workspace_bytes_for(num_heads, head_size, total_q_tokens, splits);
 }
 
 int prefill_attention_tile_bounds(const int32_t* query_start_loc, const int32_t* ctx_lens,
@@ -1087,30 +1370,26 @@ int prefill_attention_tile_bounds(const int32_t* query_start_loc, const int32_t*
                                   const int32_t* mm_ranges, int32_t num_seqs,
                                   int32_t max_q_len, int32_t max_mm_ranges,
                                   int32_t* bounds_out, hipStream_t stream) {
-  TileChoice tc;
-  int rc = choose_tiles(head_size, num_heads, num_kv_heads, &tc);
-  if (rc != PAGED_PREFILL_OK) return rc;
-  if (num_seqs < 0 || max_q_len < 0 || max_q_len > kMaxTokens || window_left < -1 ||
-      window_right < -1 || (causal != 0 && causal != 1) || max_mm_ranges < 0 ||
-      max_mm_ranges > kMaxMmRanges || (max_mm_ranges > 0 && mm_ranges == nullptr))
-    return PAGED_PREFILL_ERR_INVALID_ARG;
-  const int64_t num_q_tiles = ((int64_t)max_q_len + tc.block_q - 1) / tc.block_q;
-  const int64_t total = num_q_tiles * num_seqs;
-  if (total == 0) return PAGED_PREFILL_OK;
-  if (query_start_loc == nullptr || ctx_lens == nullptr || bounds_out == nullptr)
-    return PAGED_PREFILL_ERR_INVALID_ARG;
-  if (total > 0x7fffffffLL) return PAGED_PREFILL_ERR_UNSUPPORTED;
-  const int threads = 256;
-  const uint32_t blocks = (uint32_t)((total + threads - 1) / threads);
-  const int32_t* mm = max_mm_ranges > 0 ? mm_ranges : nullptr;
-  int ns = num_seqs, nt = (int)num_q_tiles, bq = tc.block_q, bn = tc.block_n;
-  int cz = causal, wl = window_left, wr = window_right, nr = max_mm_ranges;
-  void* args[] = {(void*)&query_start_loc, (void*)&ctx_lens, (void*)&mm, (void*)&ns,
-                  (void*)&nt, (void*)&bq, (void*)&bn, (void*)&cz, (void*)&wl, (void*)&wr,
-                  (void*)&nr, (void*)&bounds_out};
-  const hipError_t err = hipLaunchKernel((const void*)&tile_bounds_kernel, dim3(blocks),
-                                         dim3(threads), args, 0, stream);
-  return err == hipSuccess ? PAGED_PREFILL_OK : PAGED_PREFILL_ERR_HIP;
+  return run_tile_bounds(query_start_loc, ctx_lens, num_heads, num_kv_heads, head_size,
+                         window_left, window_right, causal, mm_ranges, num_seqs, max_q_len,
+                         max_mm_ranges, Options(), bounds_out, stream);
+}
+
+int prefill_attention_tile_bounds_ex(const int32_t* query_start_loc, const int32_t* ctx_lens,
+                                     int32_t num_heads, int32_t num_kv_heads,
+                                     int32_t head_size, int32_t window_left,
+                                     int32_t window_right, int32_t causal,
+                                     const int32_t* mm_ranges, int32_t num_seqs,
+                                     int32_t max_q_len, int32_t max_mm_ranges,
+                                     const int32_t* causal_per_seq, int32_t mm_clamp,
+                                     int32_t chunk_size, int32_t chunk_lookback,
+                                     int32_t* bounds_out, hipStream_t stream) {
+  return run_tile_bounds(query_start_loc, ctx_lens, num_heads, num_kv_heads, head_size,
+                         window_left, window_right, causal, mm_ranges, num_seqs, max_q_len,
+                         max_mm_ranges,
+                         make_options(causal_per_seq, mm_clamp, chunk_size, chunk_lookback, 1,
+                                      nullptr, 0),
+                         bounds_out, stream);
 }
 
 }  // extern "C"

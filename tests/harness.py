@@ -24,10 +24,17 @@ def to_device(w, cache_only=False, device="cuda"):
                 v_new=None if cache_only else bf(w.v_new), k_cache=bf(w.k_cache),
                 v_cache=bf(w.v_cache), block_table=i32(w.block_table),
                 query_start_loc=i32(w.query_start_loc), ctx_lens=i32(w.ctx_lens),
-                mm_ranges=None if w.mm_ranges is None else i32(w.mm_ranges))
+                mm_ranges=None if w.mm_ranges is None else i32(w.mm_ranges),
+                causal_per_seq=None if w.causal_per_seq is None else i32(w.causal_per_seq))
 
 
-def run_gpu(w, dev=None, cache_only=False, out=None, mm_ranges="default"):
+def variant_kwargs(w, dev, kv_splits=1):
+    """Keyword arguments of the binding for the workload's mask variant."""
+    return dict(causal_per_seq=dev["causal_per_seq"], mm_clamp=w.mm_clamp,
+                chunk_size=w.chunk_size, chunk_lookback=w.chunk_lookback, kv_splits=kv_splits)
+
+
+def run_gpu(w, dev=None, cache_only=False, out=None, mm_ranges="default", kv_splits=1):
     import paged_kv_prefill_attention_amd as ppa
     if dev is None:
         dev = to_device(w, cache_only=cache_only)
@@ -36,7 +43,7 @@ def run_gpu(w, dev=None, cache_only=False, out=None, mm_ranges="default"):
         dev["q"], dev["k_new"], dev["v_new"], dev["k_cache"], dev["v_cache"],
         dev["block_table"], dev["query_start_loc"], dev["ctx_lens"], w.num_heads,
         w.num_kv_heads, w.head_size, w.page_size, w.window_left, w.window_right, w.causal,
-        mm, w.scale, out=out, max_q_len=w.max_q_len)
+        mm, w.scale, out=out, max_q_len=w.max_q_len, **variant_kwargs(w, dev, kv_splits))
 
 
 def out_to_f32(out):
@@ -50,8 +57,8 @@ def oracle_rows(w, s, rows, heads=None, cache_only=False, mm_ranges="default"):
         w.f32("q"), None if cache_only else w.f32("k_new"),
         None if cache_only else w.f32("v_new"), w.f32("k_cache"), w.f32("v_cache"),
         w.block_table, w.query_start_loc, w.ctx_lens, w.num_heads, w.num_kv_heads,
-        w.head_size, w.page_size, w.window_left, w.window_right, w.causal, mm, w.scale, s,
-        rows, heads=heads)
+        w.head_size, w.page_size, w.window_left, w.window_right, w.causal_arg, mm, w.scale, s,
+        rows, heads=heads, **w.mask_kwargs())
 
 
 def oracle_full(w, cache_only=False):
@@ -59,8 +66,8 @@ def oracle_full(w, cache_only=False):
         w.f32("q"), None if cache_only else w.f32("k_new"),
         None if cache_only else w.f32("v_new"), w.f32("k_cache"), w.f32("v_cache"),
         w.block_table, w.query_start_loc, w.ctx_lens, w.num_heads, w.num_kv_heads,
-        w.head_size, w.page_size, w.window_left, w.window_right, w.causal, w.mm_ranges,
-        w.scale)
+        w.head_size, w.page_size, w.window_left, w.window_right, w.causal_arg, w.mm_ranges,
+        w.scale, **w.mask_kwargs())
 
 
 def compare(gpu, ref, what=""):

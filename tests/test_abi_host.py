@@ -113,3 +113,36 @@ def test_strerror(lib):
     assert "invalid" in ppa.strerror(-1)
     assert "unsupported" in ppa.strerror(-2)
     assert "unknown" in ppa.strerror(7)
+
+
+def test_invalid_ex_options_return_before_launch(lib):
+    # option checks run on the host before any pointer is touched or kernel launched
+    P = [None] * 8
+    common = (8, 2, 128, 16, -1, -1, 1, None, 0.1, None, 0, 0, 0, 1, 1, 0)
+    # empty batch with valid options: OK without a launch
+    assert lib.prefill_attention_ex(*P, *common, None, 1, 0, -1, 1, None, 0, None) == 0
+    # non-null stand-in pointers (never dereferenced: every case fails a host check)
+    import ctypes
+    F = [ctypes.c_void_p(4096 * (i + 1)) for i in range(8)]
+    nonempty = (8, 2, 128, 16, -1, -1, 1, None, 0.1, ctypes.c_void_p(1 << 20), 1, 10, 10, 1,
+                1, 0)
+    for bad in [(None, 2, 0, -1, 1), (None, 1, -1, -1, 1), (None, 1, 16, -2, 1),
+                (None, 1, 0, -1, -1), (None, 1, 0, -1, 65),
+                (None, 1, 0, -1, 4)]:  # four splits without a workspace
+        rc = lib.prefill_attention_ex(*F, *nonempty, *bad, None, 0, None)
+        assert rc == ppa.ERR_INVALID_ARG, bad
+
+
+def test_split_count_and_workspace_size(lib):
+    # explicit counts pass through; automatic splits only small batches
+    assert ppa.split_count(128, 64, 64, 8, 873, 1) == 1
+    assert ppa.split_count(128, 64, 64, 8, 873, 5) == 5
+    assert ppa.split_count(128, 64, 64, 8, 873, 0) == 1        # 8*64*4 = 2048 items
+    assert ppa.split_count(128, 32, 8, 2, 256, 0) == 8         # 2*8*4 = 64 items -> 512/64
+    assert ppa.split_count(64, 8, 8, 1, 64, 0) == 16           # 8 items, capped at 16
+    with pytest.raises(ppa.PrefillError):
+        ppa.split_count(128, 8, 8, 1, 64, 65)
+    assert ppa.workspace_size(8, 128, 100, 1) == 0
+    rows = 3 * 100 * 8
+    o_bytes = -(-(rows * 128 * 4) // 256) * 256
+    assert ppa.workspace_size(8, 128, 100, 3) == o_bytes + rows * 8
