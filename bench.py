@@ -86,6 +86,35 @@ def time_launches(fn, steps: int, warmup: int):
     return span / steps, per, wall
 
 
+def time_graph(fn, steps: int, warmup: int, reps: int = 10):
+    """Device time per launch: ``reps`` launches captured in one HIP graph, the
+    graph replayed ``steps`` times between events (no host gaps between
+    launches, which dominate small workloads when launched eagerly)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(reps):
+                fn()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / (steps * reps)
+    del g
+    return ms
+
+
 def to_device(w, cache_only=False):
     """Upload a seeded workload (bf16 bit patterns, int32 metadata) to cuda:0."""
     import numpy as np
@@ -102,38 +131,57 @@ def to_device(w, cache_only=False):
                 v_new=None if cache_only else bf(w.v_new), k_cache=bf(w.k_cache),
                 v_cache=bf(w.v_cache), block_table=i32(w.block_table),
                 query_start_loc=i32(w.query_start_loc), ctx_lens=i32(w.ctx_lens),
-                mm_ranges=None if w.mm_ranges is None else i32(w.mm_ranges))
+                mm_ranges=None if w.mm_ranges is None else i32(w.mm_ranges),
+                causal_per_seq=None if w.causal_per_seq is None else i32(w.causal_per_seq))
 
 
-def make_launcher(w, cache_only=False):
+def make_launcher(w, cache_only=False, kv_splits=1):
+    """A closure launching the library on the resident workload.  Split-KV gets its
+    workspace once, outside the timed launches."""
     import torch
     import paged_kv_prefill_attention_amd as ppa
     dev = to_device(w, cache_only=cache_only)
     out = torch.empty_like(dev["q"])
+    k = ppa.split_count(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs, w.max_q_len,
+                        kv_splits)
+    need = ppa.workspace_size(w.num_heads, w.head_size, w.total_q_tokens, k)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+    dev["workspace"] = ws
+    extra = dict(causal_per_seq=dev["causal_per_seq"], mm_clamp=w.mm_clamp,
+                 chunk_size=w.chunk_size, chunk_lookback=w.chunk_lookback,
+                 kv_splits=kv_splits, workspace=ws)
 
     def fn():
         ppa.prefill_attention(dev["q"], dev["k_new"], dev["v_new"], dev["k_cache"],
                               dev["v_cache"], dev["block_table"], dev["query_start_loc"],
                               dev["ctx_lens"], w.num_heads, w.num_kv_heads, w.head_size,
                               w.page_size, w.window_left, w.window_right, w.causal,
-                              dev["mm_ranges"], w.scale, out=out, max_q_len=w.max_q_len)
+                              dev["mm_ranges"], w.scale, out=out, max_q_len=w.max_q_len,
+                              **extra)
     return fn, dev, out
 
 
 def count_useful_pairs(w) -> int:
     """Allowed (query row, key) pairs for one query head.  Each query's allowed
     keys form one interval holding its own position: the base window
-    [a - window_left, a | a + window_right | L-1], widened by every valid
-    multimodal range [st, en] (st < en) that holds the query, whose left edge
-    is clamped to the window; then clamped to [0, L-1]."""
+    [left edge, a | a + window_right | L-1] (left edge: a - window_left, or the
+    chunk start with lookback under chunked local attention), widened by every
+    valid multimodal range [st, en] (st < en) that holds the query, whose left
+    edge is clamped to the window unless the clamp is off; then clamped to
+    [0, L-1].  The causal flag may be per sequence."""
     import numpy as np
     total = 0
+    chunked = w.chunk_size > 0 and w.chunk_lookback >= 0
     for s in range(w.num_seqs):
         c, n = int(w.ctx_lens[s]), int(w.q_lens[s])
         L = c + n
         a = c + np.arange(n, dtype=np.int64)
-        lo = a - w.window_left if w.window_left >= 0 else np.zeros_like(a)
-        if w.causal:
+        causal = w.causal if w.causal_per_seq is None else bool(w.causal_per_seq[s])
+        if chunked:
+            lo = (a // w.chunk_size - w.chunk_lookback) * w.chunk_size
+        else:
+            lo = a - w.window_left if w.window_left >= 0 else np.zeros_like(a)
+        if causal:
             hi = a.copy()
         elif w.window_right >= 0:
             hi = a + w.window_right
@@ -142,7 +190,8 @@ def count_useful_pairs(w) -> int:
         for st, en in w.mm_list(s):
             if st < en:
                 hold = (a >= st) & (a <= en)
-                left = np.maximum(st, a - w.window_left) if w.window_left >= 0 else st
+                clamp = w.mm_clamp and w.window_left >= 0
+                left = np.maximum(st, a - w.window_left) if clamp else st
                 lo = np.where(hold, np.minimum(lo, left), lo)
                 hi = np.where(hold, np.maximum(hi, en), hi)
         lo, hi = np.maximum(lo, 0), np.minimum(hi, L - 1)
@@ -155,8 +204,9 @@ def useful_flop(w) -> int:
     return 4 * w.head_size * w.num_heads * count_useful_pairs(w)
 
 
-def cpu_baseline(w, heads: int):
-    """Time the CPU oracle (as it stands) on heads [0, heads) of every sequence."""
+def cpu_baseline(w, heads: int, min_seconds: float = 10.0, max_passes: int = 8):
+    """Time the CPU oracle (as it stands) on heads [0, heads) of every sequence,
+    repeating whole passes until at least ``min_seconds`` have elapsed."""
     import numpy as np
     import oracle
     try:
@@ -169,36 +219,54 @@ def cpu_baseline(w, heads: int):
             w.head_size, w.page_size, w.window_left, w.window_right, w.causal, w.mm_ranges,
             w.scale)
     t0 = time.perf_counter()
-    for s in range(w.num_seqs):
-        n = int(w.q_lens[s])
-        if n:
-            oracle.reference_rows(*args, s, np.arange(n), heads=range(heads))
+    passes = 0
+    while passes < max_passes:
+        for s in range(w.num_seqs):
+            n = int(w.q_lens[s])
+            if n:
+                oracle.reference_rows(*args, s, np.arange(n), heads=range(heads))
+        passes += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
     el = time.perf_counter() - t0
-    flop = useful_flop(w) * heads // w.num_heads
+    flop = useful_flop(w) * heads // w.num_heads * passes
     return {"value": flop / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": "fp32 numpy oracle, query heads 0..%d of all %d sequences (all rows), "
-                      "%.1f s, %.3g useful FLOP; host %s, os.cpu_count()=%s, affinity=%d" % (
-                          heads - 1, w.num_seqs, el, flop, platform.processor() or "cpu",
-                          os.cpu_count(), len(os.sched_getaffinity(0)))}
+                      "%d pass(es), %.1f s, %.3g useful FLOP; host %s, os.cpu_count()=%s, "
+                      "affinity=%d, BLAS threads %d" % (
+                          heads - 1, w.num_seqs, passes, el, flop,
+                          platform.processor() or "cpu", os.cpu_count(),
+                          len(os.sched_getaffinity(0)), threads)}
 
 
 def run_suite(path, steps, warmup):
     """Every configuration plus the sliding-window length sweep."""
     import torch
-    from workloads import make_config
+    from workloads import NAMED, make_config, make_named
     rows = []
     cases = [(1, None, None), (2, None, None), (3, 1040, None), (3, 1056, None),
              (4, None, None), (5, None, None)]
     cases += [(4, None, n) for n in (2048, 4096, 8192, 16384, 32768, 65536)]
-    for cid, P, n in cases:
-        w = make_config(cid, page_size=P, new_tokens=n)
-        fn, dev, out = make_launcher(w)
+    cases = [(cid, P, n, 1) for cid, P, n in cases]
+    # split-KV: explicit and automatic counts, beside the unsplit launch
+    cases += [(3, 1040, None, 2), (3, 1040, None, 4)]
+    cases += [(name, None, None, k) for name in NAMED for k in
+              ((1, 0) if name == "long_context_short_chunk" else (1,))]
+    for cid, P, n, splits in cases:
+        w = make_named(cid) if isinstance(cid, str) else make_config(cid, page_size=P,
+                                                                      new_tokens=n)
+        fn, dev, out = make_launcher(w, kv_splits=splits)
         ms, per, _ = time_launches(fn, steps, warmup)
         per.sort()
+        ms_dev = time_graph(fn, max(3, steps // 5), 2)
         flop = useful_flop(w)
+        import paged_kv_prefill_attention_amd as ppa
+        k = ppa.split_count(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs,
+                            w.max_q_len, splits)
         rec = {"config": cid, "workload": w.name, "new_tokens": int(w.q_lens.sum()),
-               "ms_mean": ms, "ms_median": per[len(per) // 2],
+               "kv_splits": k, "ms_mean": ms, "ms_median": per[len(per) // 2],
+               "ms_device": ms_dev, "device_tflops": flop / (ms_dev / 1e3) / 1e12,
                "useful_tflops": flop / (ms / 1e3) / 1e12,
                "frac_mfma_peak": flop / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
                "alg_gbs": algorithmic_bytes(w) / (ms / 1e3) / 1e9, "useful_flop": flop}
@@ -216,7 +284,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-heads", type=int, default=16,
+    ap.add_argument("--cpu-heads", type=int, default=64,
                     help="query heads in the bounded CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", default=None, help="also time every config; write JSON lines")

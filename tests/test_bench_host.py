@@ -9,7 +9,7 @@ import numpy as np
 
 import bench
 import oracle
-from workloads import make_config, make_workload
+from workloads import NAMED, make_config, make_named, make_workload
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -28,10 +28,15 @@ def test_useful_pairs_counter_matches_oracle():
                                 q_lens=rng.integers(1, 150, S), num_heads=2, num_kv_heads=1,
                                 head_size=8, page_size=16, causal=bool(i % 3),
                                 window_left=int(rng.choice([-1, 0, 9, 70])),
-                                window_right=int(rng.choice([-1, 0, 5, 90])), mm_ranges=mm))
+                                window_right=int(rng.choice([-1, 0, 5, 90])), mm_ranges=mm,
+                                causal_per_seq=rng.integers(0, 2, S) if i % 4 == 1 else None,
+                                mm_clamp=bool(i % 5), chunk_size=int(rng.choice([0, 16, 50])),
+                                chunk_lookback=int(rng.choice([-1, 0, 2]))))
+    ws += [make_named(n) for n in NAMED]
     for w in ws:
         assert bench.count_useful_pairs(w) == oracle.useful_pairs(
-            w.ctx_lens, w.q_lens, w.causal, w.window_left, w.window_right, w.mm_ranges)
+            w.ctx_lens, w.q_lens, w.causal_arg, w.window_left, w.window_right, w.mm_ranges,
+            **w.mask_kwargs()), w.name
 
 
 def test_bench_refuses_multi_gpu():

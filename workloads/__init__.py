@@ -12,6 +12,8 @@ from .synth import (  # noqa: F401
     Workload,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
+    NAMED,
     make_config,
+    make_named,
     make_workload,
 )

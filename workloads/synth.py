@@ -271,3 +271,34 @@ def make_config(cid: int, *, page_size: Optional[int] = None, new_tokens: Option
                          causal=spec["causal"], window_left=spec["wl"], window_right=spec["wr"],
                          mm_ranges=mm, new_in_cache=new_in_cache,
                          block_table_override=override, name=name, rng=rng)
+
+
+# Workloads of the extended rows (mask variants and split-KV), seeded like the
+# benchmark configurations.  Shapes: a short chunk after a long cached context
+# (few Q tiles, the split-KV case); a long sequence under chunked local
+# attention with one chunk of lookback; the multimodal workload with its
+# ranges unclamped; the ragged batch with a causal flag per sequence.
+def make_named(name: str) -> Workload:
+    if name == "long_context_short_chunk":
+        return make_workload(seed=2001, ctx_lens=[32768, 30000], q_lens=[256, 200],
+                             num_heads=32, num_kv_heads=8, head_size=128, page_size=16,
+                             causal=True, name=name)
+    if name == "chunked_local_16k":
+        return make_workload(seed=2002, ctx_lens=[0], q_lens=[16384], num_heads=16,
+                             num_kv_heads=4, head_size=128, page_size=16, causal=True,
+                             chunk_size=4096, chunk_lookback=1, name=name)
+    if name == "window_mm_prefix_unclamped":
+        w = make_config(5)
+        w.name = name
+        w.mm_clamp = False
+        return w
+    if name == "ragged_batch_per_seq_causal":
+        w = make_config(2)
+        w.name = name
+        w.causal_per_seq = np.array([1, 0, 1, 1, 0, 1, 0, 1], dtype=np.int32)
+        return w
+    raise KeyError(name)
+
+
+NAMED = ["long_context_short_chunk", "chunked_local_16k", "window_mm_prefix_unclamped",
+         "ragged_batch_per_seq_causal"]
