@@ -529,6 +529,8 @@ void prefill_attention_kernel(const KernelArgs p) {
   }
   block_barrier();
 
+  int cached_pg = -1;        // page index whose element base is cached_base (wave-uniform)
+  int64_t cached_base = 0;
   auto issue_tile = [&](int tile, int stage) __attribute__((always_inline)) {
     const int j0 = tile * BN;
     const uint32_t kst = smem_base + (uint32_t)(stage * 2 * TILE_ELEMS * 2);
@@ -543,8 +545,14 @@ void prefill_attention_kernel(const KernelArgs p) {
       const uint16_t* kb = nullptr;
       const uint16_t* vb = nullptr;
       if (ws + WROWS <= cache_end && slot + WROWS <= p.page_size) {
-        const int page = __builtin_amdgcn_readfirstlane(bt_cache[pg - pg_base]);
-        const int64_t off = ((int64_t)page * p.page_size + slot) * kv_row_stride + (int64_t)g * D;
+        // Consecutive tiles mostly stay in the same page: look the page up
+        // only when it changes.
+        if (pg != cached_pg) {
+          const int page = __builtin_amdgcn_readfirstlane(bt_cache[pg - pg_base]);
+          cached_base = (int64_t)page * p.page_size * kv_row_stride + (int64_t)g * D;
+          cached_pg = pg;
+        }
+        const int64_t off = cached_base + (int64_t)slot * kv_row_stride;
         kb = kc_ptr + off;
         vb = vc_ptr + off;
       } else if (ws >= cache_end && ws + WROWS <= L) {
