@@ -47,6 +47,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) float lds_f32;
 
 constexpr int kMaxTokens = 1 << 24; // positions per sequence the resolver handles exactly
 constexpr int kMaxMmRanges = 4096;
@@ -291,9 +292,20 @@ __device__ __forceinline__ int seq_ntiles(const int32_t* qsl, int s, int block_q
   return (qsl[s + 1] - qsl[s] + block_q - 1) / block_q;
 }
 
+// Per-sequence fields staged in LDS by decode_work for batches of up to
+// kSortMaxSeqs sequences (one round trip to memory for all of them).
+struct SeqTable {
+  int order[kSortMaxSeqs];           // sequence of rank r (heaviest first)
+  int ntiles_by_rank[kSortMaxSeqs];  // its Q tile count
+  int key[kSortMaxSeqs];             // context + new tokens
+  int q0[kSortMaxSeqs];              // query_start_loc
+  int ctx[kSortMaxSeqs];             // cached tokens
+};
+
 template <typename Args>
-__device__ WorkItem decode_work(const Args& p, int b, int tid, int nthreads, int* order,
-                                int* ntiles_by_rank) {
+__device__ WorkItem decode_work(const Args& p, int b, int tid, int nthreads, SeqTable& st) {
+  int* order = st.order;
+  int* ntiles_by_rank = st.ntiles_by_rank;
   const int S = p.num_seqs;
   const int Hkv = p.num_kv_heads;
   const int HBLK = p.head_blocks;
@@ -302,14 +314,21 @@ __device__ WorkItem decode_work(const Args& p, int b, int tid, int nthreads, int
   WorkItem w{0, 0, 0, 0, false};
   if (S <= kSortMaxSeqs) {
     for (int i = tid; i < S; i += nthreads) {
-      const int key_i = p.ctx_lens[i] + p.qsl[i + 1] - p.qsl[i];
+      const int a = p.qsl[i], e = p.qsl[i + 1], cl = p.ctx_lens[i];
+      st.key[i] = cl + e - a;
+      st.q0[i] = a;
+      st.ctx[i] = cl;
+    }
+    __syncthreads();
+    for (int i = tid; i < S; i += nthreads) {
+      const int key_i = st.key[i];
       int rank = 0;
       for (int j = 0; j < S; ++j) {
-        const int key_j = p.ctx_lens[j] + p.qsl[j + 1] - p.qsl[j];
+        const int key_j = st.key[j];
         rank += (key_j > key_i) || (key_j == key_i && j < i);
       }
       order[rank] = i;
-      ntiles_by_rank[rank] = seq_ntiles(p.qsl, i, p.block_q);
+      ntiles_by_rank[rank] = (key_i - st.ctx[i] + p.block_q - 1) / p.block_q;
     }
     __syncthreads();
     // group rank r = sr * Hkv + g; XCD x owns ranks r = x (mod 8)
@@ -369,6 +388,10 @@ struct TileShape {
   // Block-table entries staged in LDS per workgroup (one workgroup per CU
   // when the ring is large, two otherwise).
   static constexpr int BT_CACHE = LDS_BYTES >= 96 * 1024 ? 4096 : 2048;
+  // KV-pair mode (short Q tiles): the two halves of the workgroup exchange
+  // their partial results through the ring, NW/2 x 64 lanes x (O, m, l).
+  static constexpr int XREGS = RB * (D / 32 * 16 + 2);
+  static constexpr bool PAIR = NW % 2 == 0 && NW / 2 * 64 * XREGS * 4 <= LDS_BYTES;
   static_assert(DMA_PER_TENSOR % NW == 0, "copies must split evenly over the wavefronts");
   static_assert(BN % 32 == 0 && D % 32 == 0, "MFMA blocking");
   static_assert(NSTAGE >= 2 && NSTAGE <= 6, "ring depth");
@@ -415,22 +438,24 @@ void prefill_attention_kernel(const KernelArgs p) {
   constexpr int TILE_ELEMS = BN * D;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[NSTAGE][2][TILE_ELEMS];
 
-  __shared__ int sched_seq[kSortMaxSeqs];
-  __shared__ int sched_ntiles[kSortMaxSeqs];
+  __shared__ SeqTable seqs;
   const int tid = threadIdx.x;
   // Split-KV: the kv_splits segments of one work item take consecutive slots
   // of the same XCD.
   const int split = (int)((blockIdx.x / kNumXcd) % p.kv_splits);
   const int bitem = (int)((blockIdx.x / kNumXcd) / p.kv_splits) * kNumXcd + blockIdx.x % kNumXcd;
-  const WorkItem wi = decode_work(p, bitem, tid, C::THREADS, sched_seq, sched_ntiles);
+  const WorkItem wi = decode_work(p, bitem, tid, C::THREADS, seqs);
   if (!wi.valid) return;  // padding slot
   const int s = wi.s;
   const int g = wi.g;
   const int hblk = wi.hblk;
   const int t = wi.t;
-  const int q0 = p.qsl[s];
-  const int n = p.qsl[s + 1] - q0;
-  const int c = p.ctx_lens[s];
+  // workgroup-uniform: scalar registers (the copy bases are built from them)
+  const bool staged = p.num_seqs <= kSortMaxSeqs;
+  const int q0 = __builtin_amdgcn_readfirstlane(staged ? seqs.q0[s] : p.qsl[s]);
+  const int n = __builtin_amdgcn_readfirstlane(staged ? seqs.key[s] - seqs.ctx[s]
+                                                      : p.qsl[s + 1] - p.qsl[s]);
+  const int c = __builtin_amdgcn_readfirstlane(staged ? seqs.ctx[s] : p.ctx_lens[s]);
   const int L = c + n;
   const int cache_end = p.cache_only ? L : c;
   const int R = p.max_mm_ranges;
@@ -455,14 +480,26 @@ void prefill_attention_kernel(const KernelArgs p) {
   const int half = lane >> 5;
   const int col = lane & 31;
 
+  // ---- KV-pair mode.  When every valid row of the Q tile lies in the first
+  // half of the tile (the short last tile of a sequence), both halves of the
+  // workgroup take those rows and split the KV tiles between them, even tiles
+  // to the first half and odd to the second: half the loop steps, with all
+  // wavefronts busy.  The halves' partial results are merged at the end.
+  const int vtok = min(n - t * p.block_q, p.block_q);
+  const int rows_used = (p.heads_per_tile - 1) * p.block_q + vtok;
+  const bool pair = __builtin_amdgcn_readfirstlane(
+                        C::PAIR && rows_used <= C::ROWS / 2 && tb.y - tb.x >= 2 ? 1 : 0) != 0;
+  const int khalf = pair ? wave / (NW / 2) : 0;  // KV half: tiles with index % 2 == khalf
+  const int wrow = pair ? wave % (NW / 2) : wave;  // row block of the tile
+
   // ---- this lane's query rows, one per row block (both lane halves hold the
-  // same rows): tile row wave*32*RB + 32*rb + col
+  // same rows): tile row wrow*32*RB + 32*rb + col
   int tok[RB], head[RB], lo_a[RB], hi_a[RB];
   bool valid[RB];
   int lo_max = INT_MIN, hi_min = INT_MAX, lo_min = INT_MAX, hi_max = INT_MIN;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int row = (wave * RB + rb) * 32 + col;
+    const int row = (wrow * RB + rb) * 32 + col;
     const int hb = row / p.block_q;
     tok[rb] = t * p.block_q + (row - hb * p.block_q);
     valid[rb] = tok[rb] < n;
@@ -513,6 +550,18 @@ void prefill_attention_kernel(const KernelArgs p) {
     voff_k[qi] = (uint32_t)((rr * kv_row_stride + 8 * Lay::kslot(r, lane_slot)) * 2);
     voff_v[qi] = (uint32_t)((rr * kv_row_stride + 8 * Lay::vslot(r, lane_slot)) * 2);
   }
+  // ---- Q rows, loaded here so that their latency overlaps the block-table
+  // staging below (lane: row `col`, dims 16ks + 8half..+8).  Rows past the
+  // sequence read its first token (always present) and are zeroed after the
+  // loads: a conditional load would be waited for one at a time.
+  u32x4 qraw[RB][KSTEPS];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const uint16_t* qrow =
+        p.q + ((int64_t)(q0 + (valid[rb] ? tok[rb] : 0)) * p.num_heads + head[rb]) * D;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qraw[rb][ks] = *(const u32x4*)(qrow + 16 * ks + 8 * half);
+  }
   // Block-table entries of every page the tile loop reads, staged in LDS once,
   // so the loop resolves pages with one LDS read per lane.  Workgroups that
   // touch more than BT_CACHE pages fall back to scalar-unit block-table reads.
@@ -527,6 +576,10 @@ void prefill_attention_kernel(const KernelArgs p) {
   if (bt_in_lds) {
     for (int i = tid; i < pg_count; i += C::THREADS) bt_cache[i] = bt[pg_base + i];
   }
+  // The Q loads complete here, before any tile copy is issued: a wait for
+  // them later would also wait for copies in flight.  (The builtin form lets
+  // the compiler see it: vmcnt(0), expcnt and lgkmcnt unconstrained.)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   block_barrier();
 
   int cached_pg = -1;        // page index whose element base is cached_base (wave-uniform)
@@ -697,23 +750,16 @@ void prefill_attention_kernel(const KernelArgs p) {
   if (ntile > 0) issue_tile(tb.x, 0);
   if (ntile > 1) issue_tile(tb.x + 1, 1);
 
-  // ---- Q fragments: B operand of S^T = K Q^T (lane: row `col`, dims 16ks + 8half..+8)
+  // ---- Q fragments: B operand of S^T = K Q^T, prescaled by scale*log2(e)
   bf16x8 qf[RB][KSTEPS];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const uint16_t* qrow =
-        p.q + ((int64_t)(q0 + (valid[rb] ? tok[rb] : 0)) * p.num_heads + head[rb]) * D;
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      u32x4 v = valid[rb] ? *(const u32x4*)(qrow + 16 * ks + 8 * half) : u32x4{0, 0, 0, 0};
+      const u32x4 v = valid[rb] ? qraw[rb][ks] : u32x4{0, 0, 0, 0};
       const f32x8 x = __builtin_convertvector(__builtin_bit_cast(bf16x8, v), f32x8);
       qf[rb][ks] = __builtin_convertvector(x * p.scale_log2, bf16x8);
     }
-  }
-  // The Q loads must be complete before the tile loop, or the compiler places
-  // its wait for them inside the loop, where it would drain the copies in
-  // flight on every iteration.  (vmcnt(0), expcnt and lgkmcnt unconstrained.)
-  __builtin_amdgcn_s_waitcnt(0x0F70);
 
 
   // ---- per-tile pieces
@@ -891,18 +937,76 @@ void prefill_attention_kernel(const KernelArgs p) {
     }
   };
 
-  // One tile at a time: refill, wait for this tile's copies, publish, compute.
-  for (int it = 0; it < ntile; ++it) {
-    if (it + 2 < ntile) issue_tile(tb.x + it + 2, (it + 2) % NSTAGE);
-    wait_copies<2 * C::DMA_PER_WAVE, 2>(ntile - 1 - it);
-    block_barrier();
-    if (!tile_active(it)) continue;
-    f32x16 sacc[RB][NKB];
-    bf16x8 pf[RB][PSTEPS];
-    qk(it % NSTAGE, sacc);
-    mask_rowmax(it, sacc);
-    expsum(sacc, pf);
-    pv(it % NSTAGE, pf);
+  if (!pair) {
+    // One tile at a time: refill, wait for this tile's copies, publish, compute.
+    for (int it = 0; it < ntile; ++it) {
+      if (it + 2 < ntile) issue_tile(tb.x + it + 2, (it + 2) % NSTAGE);
+      wait_copies<2 * C::DMA_PER_WAVE, 2>(ntile - 1 - it);
+      block_barrier();
+      if (!tile_active(it)) continue;
+      f32x16 sacc[RB][NKB];
+      bf16x8 pf[RB][PSTEPS];
+      qk(it % NSTAGE, sacc);
+      mask_rowmax(it, sacc);
+      expsum(sacc, pf);
+      pv(it % NSTAGE, pf);
+    }
+  } else {
+    // Step i: half `khalf` computes tile 2i + khalf.  The copies of step i + 1
+    // go into the stages of step i - 1, so they are issued after the barrier
+    // of step i, once every wavefront has left step i - 1.
+    for (int i = 0; 2 * i < ntile; ++i) {
+      vm_wait<0>();
+      block_barrier();
+      if (2 * i + 2 < ntile) issue_tile(tb.x + 2 * i + 2, (2 * i + 2) % NSTAGE);
+      if (2 * i + 3 < ntile) issue_tile(tb.x + 2 * i + 3, (2 * i + 3) % NSTAGE);
+      const int it = 2 * i + khalf;
+      if (it >= ntile || !tile_active(it)) continue;
+      f32x16 sacc[RB][NKB];
+      bf16x8 pf[RB][PSTEPS];
+      qk(it % NSTAGE, sacc);
+      mask_rowmax(it, sacc);
+      expsum(sacc, pf);
+      pv(it % NSTAGE, pf);
+    }
+    if constexpr (C::PAIR) {
+      // Merge: the second half leaves (O, m, l) in the ring, laid out
+      // [row block][register][lane]; the first half combines them with its own,
+      // both rescaled to the larger reference max (log2 units).
+      block_barrier();  // every wavefront is done reading tiles
+      lds_f32* xb = (lds_f32*)(lds_u16*)&smem[0][0][0] + (wrow * C::XREGS) * 64 + lane;
+      if (khalf == 1) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          lds_f32* xr = xb + rb * (NDB * 16 + 2) * 64;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) xr[(db * 16 + r) * 64] = oacc[rb][db][r];
+          xr[NDB * 16 * 64] = m_run[rb];
+          xr[(NDB * 16 + 1) * 64] = l_run[rb];
+        }
+      }
+      block_barrier();
+      if (khalf == 1) return;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const lds_f32* xr = xb + rb * (NDB * 16 + 2) * 64;
+        const float m1 = xr[NDB * 16 * 64];
+        const float l1 = xr[(NDB * 16 + 1) * 64];
+        const float m0 = m_run[rb];
+        const float mn = fmaxf(m0, m1);
+        const float a0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - mn);
+        const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mn);
+        l_run[rb] = l_run[rb] * a0 + l1 * a1;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            oacc[rb][db][r] = oacc[rb][db][r] * a0 + xr[(db * 16 + r) * 64] * a1;
+        m_run[rb] = mn;
+      }
+    }
   }
 
   // ---- split-KV epilogue: the segment's unnormalised O with its reference max
