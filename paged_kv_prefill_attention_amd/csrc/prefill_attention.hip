@@ -403,20 +403,6 @@ template <> struct ShapeFor<64> { using T = TileShape<64, PREFILL_TILE_D64>; };
 template <> struct ShapeFor<128> { using T = TileShape<128, PREFILL_TILE_D128>; };
 template <> struct ShapeFor<256> { using T = TileShape<256, PREFILL_TILE_D256>; };
 
-// Wait until at most `after` later tiles' copies (PER_TILE each) are in flight.
-template <int PER_TILE, int MAX_AFTER>
-__device__ __forceinline__ void wait_copies(int after) {
-  if constexpr (MAX_AFTER > 0) {
-    if (after >= MAX_AFTER) {
-      vm_wait<PER_TILE * MAX_AFTER>();
-      return;
-    }
-    wait_copies<PER_TILE, MAX_AFTER - 1>(after);
-  } else {
-    vm_wait<0>();
-  }
-}
-
 template <typename C>
 __global__ __attribute__((amdgpu_flat_work_group_size(C::THREADS, C::THREADS),
                           amdgpu_waves_per_eu(C::WPE, C::WPE)))
@@ -741,10 +727,9 @@ void prefill_attention_kernel(const KernelArgs p) {
                                                  16 * Lay::vslot(v_row_in, v_dim_in >> 3) +
                                                  2 * (v_dim_in & 7));
 
-  // Ring protocol (NSTAGE = 4): the copies of tile i + 2 are issued at the top
-  // of iteration i, into the stage of tile i - 2, which every wavefront
-  // released before passing the previous iteration's barrier.  Two tiles are
-  // in flight while one is waited for.
+  // Ring protocol (NSTAGE = 4): tiles go in pairs, one pair per barrier.  The
+  // pair of step i + 1 is copied while step i computes, into the stages of
+  // step i - 1, which every wavefront left before the barrier of step i.
   static_assert(NSTAGE == 4, "ring protocol assumes four stages");
   const int ntile = tb.y - tb.x;
   if (ntile > 0) issue_tile(tb.x, 0);
@@ -937,13 +922,19 @@ void prefill_attention_kernel(const KernelArgs p) {
     }
   };
 
-  if (!pair) {
-    // One tile at a time: refill, wait for this tile's copies, publish, compute.
-    for (int it = 0; it < ntile; ++it) {
-      if (it + 2 < ntile) issue_tile(tb.x + it + 2, (it + 2) % NSTAGE);
-      wait_copies<2 * C::DMA_PER_WAVE, 2>(ntile - 1 - it);
-      block_barrier();
-      if (!tile_active(it)) continue;
+  // Step i covers tiles 2i and 2i + 1: both for every wavefront, or in
+  // KV-pair mode tile 2i + khalf for half khalf.  The copies of step i + 1
+  // go into the stages of step i - 1, so they are issued after the barrier
+  // of step i, once every wavefront has left step i - 1.
+  for (int i = 0; 2 * i < ntile; ++i) {
+    vm_wait<0>();
+    block_barrier();
+    if (2 * i + 2 < ntile) issue_tile(tb.x + 2 * i + 2, (2 * i + 2) % NSTAGE);
+    if (2 * i + 3 < ntile) issue_tile(tb.x + 2 * i + 3, (2 * i + 3) % NSTAGE);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int it = 2 * i + h;
+      if ((pair && h != khalf) || it >= ntile || !tile_active(it)) continue;
       f32x16 sacc[RB][NKB];
       bf16x8 pf[RB][PSTEPS];
       qk(it % NSTAGE, sacc);
@@ -951,24 +942,8 @@ void prefill_attention_kernel(const KernelArgs p) {
       expsum(sacc, pf);
       pv(it % NSTAGE, pf);
     }
-  } else {
-    // Step i: half `khalf` computes tile 2i + khalf.  The copies of step i + 1
-    // go into the stages of step i - 1, so they are issued after the barrier
-    // of step i, once every wavefront has left step i - 1.
-    for (int i = 0; 2 * i < ntile; ++i) {
-      vm_wait<0>();
-      block_barrier();
-      if (2 * i + 2 < ntile) issue_tile(tb.x + 2 * i + 2, (2 * i + 2) % NSTAGE);
-      if (2 * i + 3 < ntile) issue_tile(tb.x + 2 * i + 3, (2 * i + 3) % NSTAGE);
-      const int it = 2 * i + khalf;
-      if (it >= ntile || !tile_active(it)) continue;
-      f32x16 sacc[RB][NKB];
-      bf16x8 pf[RB][PSTEPS];
-      qk(it % NSTAGE, sacc);
-      mask_rowmax(it, sacc);
-      expsum(sacc, pf);
-      pv(it % NSTAGE, pf);
-    }
+  }
+  if (pair) {
     if constexpr (C::PAIR) {
       // Merge: the second half leaves (O, m, l) in the ring, laid out
       // [row block][register][lane]; the first half combines them with its own,
