@@ -338,12 +338,16 @@ __device__ WorkItem decode_work(const Args& p, int b, int tid, int nthreads, Seq
       const int per_group = ntiles_by_rank[sr] * HBLK;
       const int items = ng * per_group;
       if (k < items) {
-        const int gi = k / per_group;
-        const int rem = k - gi * per_group;
-        const int z = rem / HBLK;
+        // Tile-major: the ng x HBLK items of one Q tile (equal work) are
+        // consecutive, so that the round-robin dispatch over shader engines
+        // meets items of equal length.
+        const int per_tile = ng * HBLK;
+        const int z = k / per_tile;
+        const int rem = k - z * per_tile;
+        const int gi = rem / HBLK;
         w.s = order[sr];
         w.g = g0 + gi * kNumXcd;
-        w.hblk = rem - z * HBLK;
+        w.hblk = rem - gi * HBLK;
         w.t = ntiles_by_rank[sr] - 1 - z;
         w.valid = true;
         return w;
