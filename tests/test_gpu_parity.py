@@ -208,3 +208,33 @@ def test_tile_bounds_bitexact():
         ref = oracle.tile_bounds_all(w.ctx_lens, w.q_lens, bq, bn, w.causal, w.window_left,
                                      w.window_right, w.mm_ranges)
         assert np.array_equal(got.cpu().numpy(), ref), w.name
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_large_batch_without_sequence_sort(d):
+    """More sequences than the workgroup sorts in LDS (256): the work decode reads the
+    sequence table from memory and pads each (sequence, KV head) group to the
+    longest tile count.  300 short ragged sequences, whole outputs."""
+    rng = np.random.default_rng(4400 + d)
+    S = 300
+    ctx = rng.integers(0, 200, size=S)
+    ctx[rng.integers(0, S, size=20)] = 0
+    new = rng.integers(1, 60, size=S)
+    w = make_workload(seed=4401 + d, ctx_lens=ctx, q_lens=new, num_heads=4, num_kv_heads=2,
+                      head_size=d, page_size=16, causal=True, window_left=100,
+                      name="batch300_d%d" % d)
+    compare(out_to_f32(run_gpu(w)), oracle_full(w), w.name)
+
+
+@pytest.mark.parametrize("d,ctx,page", [(64, 5000, 1), (128, 9000, 1), (64, 7000, 3)])
+def test_block_table_beyond_lds_cache(d, ctx, page):
+    """A work item whose KV range covers more pages than the LDS block-table cache
+    holds (2048 entries at d=64, 4096 at d=128): pages are read on the scalar unit,
+    with copies that straddle page boundaries and the cache/new-token edge.  Whole
+    outputs, plain and split-KV."""
+    w = make_workload(seed=4500 + d + page, ctx_lens=[ctx, 40], q_lens=[200, 30],
+                      num_heads=2, num_kv_heads=1, head_size=d, page_size=page, causal=True,
+                      name="bt_fallback_d%d_P%d" % (d, page))
+    ref = oracle_full(w)
+    compare(out_to_f32(run_gpu(w)), ref, w.name)
+    compare(out_to_f32(run_gpu(w, kv_splits=3)), ref, w.name + " splits=3")
