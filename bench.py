@@ -14,6 +14,14 @@ the CPU oracle on a bounded sample of the same workload.
 
 ``--suite FILE`` additionally times every configuration and the sliding-window
 length sweep and writes them to FILE (one JSON object per line).
+
+``--tile-sweep FILE`` instead times only the tile-shape sweep workloads (one
+JSON object per workload, eager launches) with the library given by ``--lib``,
+e.g. a build with another tile shape:
+
+    python -m paged_kv_prefill_attention_amd._build \
+        --define PREFILL_TILE_D128=4,32,4,2,1 --out /tmp/lib_d128_4_32.so
+    python bench.py --lib /tmp/lib_d128_4_32.so --tile-sweep /tmp/d128_4_32.jsonl
 """
 
 from __future__ import annotations
@@ -279,6 +287,32 @@ def run_suite(path, steps, warmup):
             f.write(json.dumps(r) + "\n")
 
 
+def run_tile_sweep(path, steps, warmup):
+    """Eager timing of the tile-sweep workloads, in the order of TILE_SWEEP
+    (under a counter profiler each workload is warmup + steps dispatches)."""
+    import torch
+    from workloads import TILE_SWEEP, make_sweep
+    import paged_kv_prefill_attention_amd as ppa
+    rows = []
+    for name in TILE_SWEEP:
+        w = make_sweep(name)
+        fn, dev, out = make_launcher(w)
+        ms, per, _ = time_launches(fn, steps, warmup)
+        per.sort()
+        bq, bn = ppa.tile_config(w.head_size, w.num_heads, w.num_kv_heads)
+        flop = useful_flop(w)
+        rec = {"workload": name, "head_size": w.head_size, "block_q": bq, "block_n": bn,
+               "ms_median": per[len(per) // 2], "ms_mean": ms,
+               "useful_tflops": flop / (per[len(per) // 2] / 1e3) / 1e12}
+        rows.append(rec)
+        print(json.dumps(rec), flush=True)
+        del dev, out, fn
+        torch.cuda.empty_cache()
+    with open(path, "w") as f:
+        for r in rows:
+            f.write(json.dumps(r) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -288,6 +322,10 @@ def main():
                     help="query heads in the bounded CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--suite", default=None, help="also time every config; write JSON lines")
+    ap.add_argument("--lib", default=None,
+                    help="load this build of the library instead of the in-tree one")
+    ap.add_argument("--tile-sweep", default=None,
+                    help="only time the tile-sweep workloads; write JSON lines")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead: time a plain device copy of this many bytes (the "
                          "reference kernel for scaling the HBM byte counters)")
@@ -301,10 +339,17 @@ def main():
     import paged_kv_prefill_attention_amd as ppa
     from workloads import make_config
 
-    if not os.path.exists(ppa.library_path()):
-        ppa.build()
-    ppa.load_library()
+    if args.lib:
+        ppa.use_library(args.lib)
+    else:
+        if not os.path.exists(ppa.library_path()):
+            ppa.build()
+        ppa.load_library()
     torch.cuda.set_device(0)
+
+    if args.tile_sweep:
+        run_tile_sweep(args.tile_sweep, args.steps, args.warmup)
+        return
 
     if args.copy_bytes:
         src = torch.ones(args.copy_bytes // 2, dtype=torch.bfloat16, device="cuda")

@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     strerror,
     tile_bounds,
     tile_config,
+    use_library,
     validate,
     workspace_size,
 )

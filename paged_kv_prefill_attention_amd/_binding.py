@@ -47,11 +47,22 @@ class PrefillError(RuntimeError):
         super().__init__("%s failed: %s (%d)" % (where, strerror(code), code))
 
 
+_lib_path = None  # another build of the library to load instead (use_library)
+
+
+def use_library(path: str):
+    """Load ``path`` (another build of this library, e.g. a tile-shape variant)
+    instead of the in-tree one from now on."""
+    global _lib, _lib_path
+    _lib, _lib_path = None, path
+    return load_library()
+
+
 def load_library():
     """Load the in-tree HIP library; raise if it has not been built."""
     global _lib
     if _lib is None:
-        path = library_path()
+        path = _lib_path or library_path()
         if not os.path.exists(path):
             raise RuntimeError("HIP library %s is not built; run __graft_entry__.build()" % path)
         lib = ctypes.CDLL(path)

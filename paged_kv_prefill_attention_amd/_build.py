@@ -23,11 +23,17 @@ def library_path() -> str:
     return os.path.join(HERE, LIB_NAME)
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into ``libpagedprefill.so`` (always rebuilds)."""
-    out = library_path()
+def build(verbose: bool = False, defines=None, out=None) -> str:
+    """Compile every HIP source into ``libpagedprefill.so`` (always rebuilds).
+
+    ``defines`` (``{"PREFILL_TILE_D128": "4,32,4,2,1"}``) and ``out`` build a
+    variant of the library elsewhere, e.g. another tile shape for a sweep; the
+    in-tree library is then left as it is.
+    """
+    out = out or library_path()
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + SOURCES + ["-o", tmp]
+    dflags = ["-D%s=%s" % (k, v) for k, v in (defines or {}).items()]
+    cmd = [HIPCC] + FLAGS + dflags + SOURCES + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -43,4 +49,11 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import argparse
+    ap = argparse.ArgumentParser(description="build the HIP library (or a variant of it)")
+    ap.add_argument("--define", action="append", default=[], metavar="NAME=VALUE",
+                    help="preprocessor define, e.g. PREFILL_TILE_D128=4,32,4,2,1")
+    ap.add_argument("--out", default=None, help="output path (default: the in-tree library)")
+    a = ap.parse_args()
+    defs = dict(d.split("=", 1) for d in a.define)
+    print(build(verbose=True, defines=defs, out=a.out))

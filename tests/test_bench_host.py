@@ -9,7 +9,7 @@ import numpy as np
 
 import bench
 import oracle
-from workloads import NAMED, make_config, make_named, make_workload
+from workloads import NAMED, TILE_SWEEP, make_config, make_named, make_sweep, make_workload
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -33,6 +33,7 @@ def test_useful_pairs_counter_matches_oracle():
                                 mm_clamp=bool(i % 5), chunk_size=int(rng.choice([0, 16, 50])),
                                 chunk_lookback=int(rng.choice([-1, 0, 2]))))
     ws += [make_named(n) for n in NAMED]
+    ws += [make_sweep(n) for n in TILE_SWEEP]
     for w in ws:
         assert bench.count_useful_pairs(w) == oracle.useful_pairs(
             w.ctx_lens, w.q_lens, w.causal_arg, w.window_left, w.window_right, w.mm_ranges,
@@ -44,3 +45,20 @@ def test_bench_refuses_multi_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_variant_build_command_line(tmp_path):
+    """The build step takes preprocessor defines and an output path (tile-shape
+    variants for sweeps) and leaves the in-tree library alone; a static check of
+    the kernel rejects a shape whose copies do not split over its wavefronts."""
+    from paged_kv_prefill_attention_amd import _build
+    lib = _build.library_path()
+    before = os.path.getmtime(lib) if os.path.exists(lib) else None
+    out = str(tmp_path / "lib_variant.so")
+    r = subprocess.run([sys.executable, "-m", "paged_kv_prefill_attention_amd._build",
+                        "--define", "PREFILL_TILE_D64=8,32,4,2,1", "--out", out],
+                       capture_output=True, text=True, timeout=600, cwd=ROOT)
+    assert r.returncode != 0 and "copies must split evenly" in (r.stdout + r.stderr)
+    assert not os.path.exists(out)
+    after = os.path.getmtime(lib) if os.path.exists(lib) else None
+    assert before == after

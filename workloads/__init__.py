@@ -13,7 +13,9 @@ from .synth import (  # noqa: F401
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     NAMED,
+    TILE_SWEEP,
     make_config,
     make_named,
+    make_sweep,
     make_workload,
 )

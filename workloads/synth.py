@@ -297,7 +297,32 @@ def make_named(name: str) -> Workload:
         w.name = name
         w.causal_per_seq = np.array([1, 0, 1, 1, 0, 1, 0, 1], dtype=np.int32)
         return w
+    if name == "ragged_batch_page544_d64":
+        c2 = make_config(2)
+        return make_workload(seed=2003, ctx_lens=c2.ctx_lens, q_lens=c2.q_lens, num_heads=64,
+                             num_kv_heads=64, head_size=64, page_size=544, causal=True,
+                             name=name)
+    if name == "dense_noncausal_d128":
+        return make_workload(seed=2004, ctx_lens=[0, 0], q_lens=[8192, 8192], num_heads=32,
+                             num_kv_heads=8, head_size=128, page_size=64, causal=False,
+                             name=name)
     raise KeyError(name)
+
+
+# Workloads a tile-shape sweep times: the benchmark shapes of each head size,
+# the ragged batch at head size 64, and a dense non-causal batch (no masking,
+# no ragged tails) that isolates the tile loop.
+TILE_SWEEP = ["ragged_batch_page544", "gqa_d256_page1040", "sliding_window_16k",
+              "window_clamped_mm_prefix", "ragged_batch_page544_d64", "dense_noncausal_d128"]
+
+
+def make_sweep(name: str) -> Workload:
+    configs = {"ragged_batch_page544": (2, None), "gqa_d256_page1040": (3, 1040),
+               "sliding_window_16k": (4, None), "window_clamped_mm_prefix": (5, None)}
+    if name in configs:
+        cid, P = configs[name]
+        return make_config(cid, page_size=P)
+    return make_named(name)
 
 
 NAMED = ["long_context_short_chunk", "chunked_local_16k", "window_mm_prefix_unclamped",
