@@ -3,21 +3,24 @@
 // One workgroup owns one Q tile: `block_q` query tokens of one sequence times
 // the `heads_per_tile` query heads of one GQA group, packed into 32 MFMA rows
 // per wavefront (256 rows for 8 wavefronts), so one K/V gather serves every
-// head of the group.  The workgroup walks the KV tiles [lo, hi) given by the
-// tile bound calculator (the window unioned with every multimodal range that
-// overlaps the tile's queries; vLLM PR #50776 report, "Key source snippets";
-// vLLM PR #53147 report, "Implementation breakdown" item 2).  Per KV tile:
+// head of the group.  Work items are ranked heavy-first and keep all Q tiles
+// of one (sequence, KV head) on one XCD.  The workgroup walks the KV tiles
+// [lo, hi) given by the tile bound calculator (the window unioned with every
+// multimodal range that overlaps the tile's queries; vLLM PR #50776 report,
+// "Key source snippets"; vLLM PR #53147 report, "Implementation breakdown"
+// item 2).  Per KV tile:
 //
 //   1. page-offset resolver: key position j < ctx_len is slot j % P of page
 //      block_table[j / P] (division by an invariant integer with a
-//      Granlund-Montgomery multiply-shift, PLDI 1994; block-table entries are
-//      fetched on the scalar unit), j >= ctx_len is a row of the chunk's new
-//      K/V, j >= L reads a zero row; tiles never depend on pages, so any page
-//      size works (vLLM PR #54194 report, "Features and motivation");
+//      Granlund-Montgomery multiply-shift, PLDI 1994; the block-table entries
+//      an item reads are staged in LDS once, or read on the scalar unit when
+//      there are too many), j >= ctx_len is a row of the chunk's new K/V,
+//      j >= L reads a zero row; tiles never depend on pages, so any page size
+//      works (vLLM PR #54194 report, "Features and motivation");
 //   2. coalesced gather: 16-byte global->LDS DMA (global_load_lds_dwordx4)
-//      into a ring of NSTAGE tile buffers, so NSTAGE-1 tiles are in flight
-//      while one is consumed; one barrier per tile.  K and V rows are stored
-//      row-major with XOR-swizzled 16-byte chunks (conflict-free reads);
+//      into a 4-stage ring, two tiles per barrier with the next two in
+//      flight.  K and V rows are stored row-major with XOR-swizzled 16-byte
+//      chunks (conflict-free reads);
 //   3. S^T = K Q^T on v_mfma_f32_32x32x16_bf16: every lane holds one query
 //      row's scores, so softmax row reductions are in-lane plus one
 //      v_permlane32_swap with the lane 32 away;
@@ -27,7 +30,10 @@
 //   6. O^T += V^T P^T on the same MFMA: P rounded to bf16 (round-to-nearest-
 //      even, v_cvt_pk_bf16_f32); the V^T operand comes straight from the
 //      row-major V tile through ds_read_b64_tr_b16.
-// The epilogue divides by the row sum and stores bf16.
+// A Q tile with at most half its rows valid splits its KV tiles between the
+// two halves of the workgroup and merges them by log-sum-exp.  The epilogue
+// divides by the row sum and stores bf16 (or, under split-KV, the unnormalised
+// partial with its max and sum for merge_splits_kernel).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
