@@ -3,8 +3,8 @@
 // One workgroup owns one Q tile: `block_q` query tokens of one sequence times
 // the `heads_per_tile` query heads of one GQA group, packed into 32 MFMA rows
 // per wavefront (256 rows for 8 wavefronts), so one K/V gather serves every
-// head of the group.  Work items are ranked heavy-first and keep all Q tiles
-// of one (sequence, KV head) on one XCD.  The workgroup walks the KV tiles
+// head of the group.  Work items are ranked heavy-first and dealt
+// round-robin over the XCDs.  The workgroup walks the KV tiles
 // [lo, hi) given by the tile bound calculator (the window unioned with every
 // multimodal range that overlaps the tile's queries; vLLM PR #50776 report,
 // "Key source snippets"; vLLM PR #53147 report, "Implementation breakdown"
@@ -337,28 +337,26 @@ __device__ WorkItem decode_work(const Args& p, int b, int tid, int nthreads, Seq
       ntiles_by_rank[rank] = (key_i - st.ctx[i] + p.block_q - 1) / p.block_q;
     }
     __syncthreads();
-    // group rank r = sr * Hkv + g; XCD x owns ranks r = x (mod 8)
+    // Items in heavy-first order (sequences by length; within a sequence the
+    // last Q tile first, the KV heads and head blocks of one Q tile together)
+    // are dealt round-robin over the XCDs: slot k of XCD x is item 8k + x.
+    // Consecutive items of one Q tile are equal work, which suits the strict
+    // rotation in which an XCD hands its workgroups to its shader engines.
+    int j = k * kNumXcd + x;
     for (int sr = 0; sr < S; ++sr) {
-      const int g0 = ((x - sr * Hkv) % kNumXcd + kNumXcd) % kNumXcd;  // first g of this XCD
-      const int ng = g0 < Hkv ? (Hkv - 1 - g0) / kNumXcd + 1 : 0;
-      const int per_group = ntiles_by_rank[sr] * HBLK;
-      const int items = ng * per_group;
-      if (k < items) {
-        // Tile-major: the ng x HBLK items of one Q tile (equal work) are
-        // consecutive, so that the round-robin dispatch over shader engines
-        // meets items of equal length.
-        const int per_tile = ng * HBLK;
-        const int z = k / per_tile;
-        const int rem = k - z * per_tile;
-        const int gi = rem / HBLK;
+      const int per_tile = Hkv * HBLK;
+      const int per_seq = per_tile * ntiles_by_rank[sr];
+      if (j < per_seq) {
+        const int z = j / per_tile;
+        const int rem = j - z * per_tile;
         w.s = order[sr];
-        w.g = g0 + gi * kNumXcd;
-        w.hblk = rem - gi * HBLK;
+        w.g = rem / HBLK;
+        w.hblk = rem - w.g * HBLK;
         w.t = ntiles_by_rank[sr] - 1 - z;
         w.valid = true;
         return w;
       }
-      k -= items;
+      j -= per_seq;
     }
     return w;
   }
@@ -437,8 +435,15 @@ void prefill_attention_kernel(const KernelArgs p) {
   __shared__ SeqTable seqs;
   const int tid = threadIdx.x;
   // Split-KV: the kv_splits segments of one work item take consecutive slots
-  // of the same XCD.
-  const int split = (int)((blockIdx.x / kNumXcd) % p.kv_splits);
+  // of the same XCD.  Items that stay whole use only their segment-0 slot, and
+  // the hardware hands an XCD's workgroups to its 4 shader engines in strict
+  // rotation, so the segment-0 slot is placed per item such that those slots
+  // fall on every engine in turn.
+  const int ks = p.kv_splits;
+  const int pos = (int)((blockIdx.x / kNumXcd) % ks);
+  const int item_idx = (int)((blockIdx.x / kNumXcd) / ks);
+  const int pos0 = ks % 2 ? 0 : (ks % 4 == 2 ? (item_idx / 2) % 2 : item_idx % 4);
+  const int split = (pos + ks - pos0) % ks;
   const int bitem = (int)((blockIdx.x / kNumXcd) / p.kv_splits) * kNumXcd + blockIdx.x % kNumXcd;
   const WorkItem wi = decode_work(p, bitem, tid, C::THREADS, seqs);
   if (!wi.valid) return;  // padding slot
@@ -462,10 +467,25 @@ void prefill_attention_kernel(const KernelArgs p) {
                        p.window_left, p.window_right, p.chunk_size, p.chunk_lookback,
                        p.mm_clamp};
   int2 tb = kv_tile_range(c, n, t, p.block_q, BN, mspec, ranges, R);
-  if (p.kv_splits > 1) {  // this item's segment of the tile range (possibly empty)
-    const int per = (tb.y - tb.x + p.kv_splits - 1) / p.kv_splits;
-    const int x0 = min(tb.x + split * per, tb.y);
-    tb = make_int2(x0, min(x0 + per, tb.y));
+  // Split-KV: an item of at most `cap` KV tiles stays whole (its segment 0
+  // writes the output; the item's other slots exit).  Longer items are cut into
+  // segments of max(cap, ceil(tiles / kv_splits)) tiles, merged afterwards.
+  // cap = ceil(tiles of the longest sequence / kv_splits), so only the items
+  // that would hold back the tail are split and pay for partial results.
+  bool whole = true;
+  if (p.kv_splits > 1) {
+    const int k = p.kv_splits;
+    const int n_item = tb.y - tb.x;
+    const int lmax = staged ? seqs.key[seqs.order[0]] : 0;  // heaviest sequence first
+    const int cap = ((lmax + BN - 1) / BN + k - 1) / k;
+    const int per = max(cap, (n_item + k - 1) / k);
+    whole = __builtin_amdgcn_readfirstlane(n_item <= per ? 1 : 0) != 0;
+    if (whole) {
+      if (split > 0) return;
+    } else {  // this item's segment of the tile range (possibly empty)
+      const int x0 = min(tb.x + split * per, tb.y);
+      tb = make_int2(x0, min(x0 + per, tb.y));
+    }
   }
   // wave-uniform: keeps the loop bounds and copy bases in scalar registers
   tb.x = __builtin_amdgcn_readfirstlane(tb.x);
@@ -996,7 +1016,7 @@ void prefill_attention_kernel(const KernelArgs p) {
 
   // ---- split-KV epilogue: the segment's unnormalised O with its reference max
   // m and sum l (log2 units), merged by merge_splits_kernel.
-  if (p.kv_splits > 1) {
+  if (!whole) {
     const int64_t rows = (int64_t)p.total_q_tokens * p.num_heads;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -1022,6 +1042,10 @@ void prefill_attention_kernel(const KernelArgs p) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float l_tot = pair_sum(l_run[rb]);
+    if (p.kv_splits > 1 && valid[rb] && half == 0) {
+      // a whole item under split-KV: tell the merge that this row is final
+      p.part_ml[(int64_t)(q0 + tok[rb]) * p.num_heads + head[rb]] = make_float2(0.f, -1.f);
+    }
     if (valid[rb]) {
       const float inv = 1.f / l_tot;
       uint16_t* orow = p.out + ((int64_t)(q0 + tok[rb]) * p.num_heads + head[rb]) * D;
@@ -1058,7 +1082,8 @@ __global__ void tile_bounds_kernel(const int32_t* qsl, const int32_t* ctx_lens,
 
 // Split-KV merge (log-sum-exp rule): for each (token, head) row,
 //   out = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k,  M = max over segments
-// with l_k > 0.  One thread per 8 output dims.
+// with l_k > 0.  Rows that segment 0 marked with l = -1 belong to an item that
+// was not split; the attention kernel wrote them.  One thread per 8 output dims.
 template <int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
 void merge_splits_kernel(const float* part_o, const float2* part_ml, uint16_t* out,
@@ -1068,6 +1093,8 @@ void merge_splits_kernel(const float* part_o, const float2* part_ml, uint16_t* o
   const int64_t row = gid / TPR;
   const int sub = (int)(gid - row * TPR);
   if (row >= rows) return;
+  // segment 0 marks rows whose item was not split (l = -1): already final
+  if (part_ml[row].y < 0.f) return;
   float M = -INFINITY;
   for (int k = 0; k < splits; ++k) {
     const float2 ml = part_ml[k * rows + row];
@@ -1195,10 +1222,15 @@ void page_magic(int page_size, uint32_t* magic, int* shift) {
 
 // Workgroups per split before the split factor: 8 XCDs x slots per XCD.
 int64_t item_slots(int num_seqs, int num_kv_heads, int64_t num_q_tiles, int head_blocks) {
-  // slots per XCD: every group an XCD can own, each with up to num_q_tiles tiles
-  const int64_t groups_per_xcd = num_seqs <= kSortMaxSeqs
-      ? (int64_t)num_seqs * ((num_kv_heads + kNumXcd - 1) / kNumXcd)
-      : ((int64_t)num_seqs * num_kv_heads + kNumXcd - 1) / kNumXcd;
+  if (num_seqs <= kSortMaxSeqs) {
+    // items dealt round-robin over the XCDs: at most one per (sequence, KV
+    // head, Q tile, head block), rounded up to whole rounds
+    const int64_t items = (int64_t)num_seqs * num_kv_heads * num_q_tiles * head_blocks;
+    return (items + kNumXcd - 1) / kNumXcd * kNumXcd;
+  }
+  // large batches: per XCD a contiguous range of (sequence, KV head) groups,
+  // each with up to num_q_tiles tiles
+  const int64_t groups_per_xcd = ((int64_t)num_seqs * num_kv_heads + kNumXcd - 1) / kNumXcd;
   return kNumXcd * groups_per_xcd * num_q_tiles * head_blocks;
 }
 
