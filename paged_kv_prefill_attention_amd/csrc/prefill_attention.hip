@@ -52,6 +52,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) float lds_f32;
 
@@ -400,6 +401,8 @@ struct TileShape {
   // their partial results through the ring, NW/2 x 64 lanes x (O, m, l).
   static constexpr int XREGS = RB * (D / 32 * 16 + 2);
   static constexpr bool PAIR = NW % 2 == 0 && NW / 2 * 64 * XREGS * 4 <= LDS_BYTES;
+  // The output tile (ROWS x D bf16) is staged through the ring for row-wise stores.
+  static constexpr bool STAGE_OUT = ROWS * D * 2 <= LDS_BYTES;
   static_assert(DMA_PER_TENSOR % NW == 0, "copies must split evenly over the wavefronts");
   static_assert(BN % 32 == 0 && D % 32 == 0, "MFMA blocking");
   static_assert(NSTAGE >= 2 && NSTAGE <= 6, "ring depth");
@@ -1038,7 +1041,59 @@ void prefill_attention_kernel(const KernelArgs p) {
     }
     return;
   }
-  // ---- epilogue: O / l -> bf16; lane holds dims 32db + 8(r/4) + 4half + r%4
+  // ---- epilogue, usual case: O / l -> bf16 staged through the (now idle)
+  // ring, one row-major block of 32 * RB rows per wavefront, so that each
+  // store writes whole rows (16 bytes per lane, D / 8 lanes per row).  A lane
+  // holds dims 32db + 8b + 4half + 0..3 of its row; 16-byte chunk c of row r
+  // sits at chunk c ^ (r % (D / 8)) of the row (conflict-free reads).
+  if constexpr (C::STAGE_OUT) {
+    if (!pair) {
+      constexpr int CH = D / 8;               // 16-byte chunks per row
+      constexpr int RPI = 64 / CH;            // rows per store instruction
+      block_barrier();                        // every wavefront is done with the ring
+      const uint32_t wbase = smem_base + (uint32_t)(wave * RB * 32 * D * 2);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float l_tot = pair_sum(l_run[rb]);
+        if (p.kv_splits > 1 && valid[rb] && half == 0)
+          p.part_ml[(int64_t)(q0 + tok[rb]) * p.num_heads + head[rb]] = make_float2(0.f, -1.f);
+        const float inv = 1.f / l_tot;
+        const int r = rb * 32 + col;
+        const uint32_t rbase = wbase + (uint32_t)(r * D * 2 + 8 * half);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int b4 = 0; b4 < 4; ++b4) {
+            const f32x16& o = oacc[rb][db];
+            const f32x4 v = {o[4 * b4] * inv, o[4 * b4 + 1] * inv, o[4 * b4 + 2] * inv,
+                             o[4 * b4 + 3] * inv};
+            const uint32_t a = rbase + (uint32_t)((((4 * db + b4) ^ (r % CH)) * 16));
+            *(lds_u32x2*)(uintptr_t)a =
+                __builtin_bit_cast(u32x2, __builtin_convertvector(v, bf16x4));
+          }
+      }
+      // Read back row-major: instruction i covers rows RPI*i + lane / CH.
+      const int ch = lane % CH;
+#pragma unroll
+      for (int i = 0; i < RB * 32 / RPI; ++i) {
+        const int r = RPI * i + lane / CH;
+        const u32x4 v = *(const lds_u32x4*)(uintptr_t)(wbase + (uint32_t)(r * D * 2 +
+                                                                     16 * (ch ^ (r % CH))));
+        const int row = wrow * RB * 32 + r;  // tile row
+        const int hb = row / p.block_q;
+        const int tk = t * p.block_q + (row - hb * p.block_q);
+        if (tk < n) {
+          const int hd = g * p.group + hblk * p.heads_per_tile + hb;
+          *(u32x4*)(p.out + ((int64_t)(q0 + tk) * p.num_heads + hd) * D + 8 * ch) = v;
+        }
+      }
+      return;
+    }
+  }
+  // ---- epilogue otherwise: O / l -> bf16.  A lane holds dims 32db + 8b + 4half + 0..3
+  // (b = 0..3) of its row.  One v_permlane32_swap per dword gives lane half 0
+  // dims 32db + 16e + 0..7 and half 1 dims 32db + 16e + 8..15 (e = 0, 1), so
+  // every store writes 16 contiguous bytes per lane and 32 per row.
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float l_tot = pair_sum(l_run[rb]);
@@ -1046,20 +1101,32 @@ void prefill_attention_kernel(const KernelArgs p) {
       // a whole item under split-KV: tell the merge that this row is final
       p.part_ml[(int64_t)(q0 + tok[rb]) * p.num_heads + head[rb]] = make_float2(0.f, -1.f);
     }
-    if (valid[rb]) {
-      const float inv = 1.f / l_tot;
-      uint16_t* orow = p.out + ((int64_t)(q0 + tok[rb]) * p.num_heads + head[rb]) * D;
+    const float inv = 1.f / l_tot;
+    uint16_t* orow = p.out + ((int64_t)(q0 + tok[rb]) * p.num_heads + head[rb]) * D;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int b4 = 0; b4 < 4; ++b4) {
-          const f32x16& o = oacc[rb][db];
+      for (int e = 0; e < 2; ++e) {
+        const f32x16& o = oacc[rb][db];
+        u32x2 w[2];  // bf16 of b = 2e and b = 2e + 1
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          const int b4 = 2 * e + bb;
           const f32x4 v = {o[4 * b4] * inv, o[4 * b4 + 1] * inv, o[4 * b4 + 2] * inv,
                            o[4 * b4 + 3] * inv};
-          const bf16x4 h = __builtin_convertvector(v, bf16x4);
-          *(u32x2*)(orow + db * 32 + 8 * b4 + 4 * half) = __builtin_bit_cast(u32x2, h);
+          w[bb] = __builtin_bit_cast(u32x2, __builtin_convertvector(v, bf16x4));
         }
-    }
+        // the first half sends b = 2e + 1 and receives its partner's b = 2e;
+        // the second half sends b = 2e and receives its partner's b = 2e + 1
+        u32x4 st;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const auto r = __builtin_amdgcn_permlane32_swap(w[0][k], w[1][k], false, false);
+          st[k] = half ? (uint32_t)r[0] : w[0][k];
+          st[2 + k] = half ? w[1][k] : (uint32_t)r[1];
+        }
+        if (valid[rb]) *(u32x4*)(orow + db * 32 + 16 * e + 8 * half) = st;
+      }
   }
 }
 
@@ -1139,8 +1206,7 @@ int gcd_int(int a, int b) {
   return a;
 }
 
-// Wavefronts per workgroup: 8 (two per SIMD) while the per-lane state fits 256
-// registers, 4 (one per SIMD, 512 registers) for head size 256.
+// Query rows and keys per KV tile of the shape compiled for a head size.
 template <int D> void shape_of(int* rows, int* bn) {
   *rows = ShapeFor<D>::T::ROWS;
   *bn = ShapeFor<D>::T::BN;
