@@ -508,8 +508,12 @@ void prefill_attention_kernel(const KernelArgs p) {
   const int rows_used = (p.heads_per_tile - 1) * p.block_q + vtok;
   const bool pair = __builtin_amdgcn_readfirstlane(
                         C::PAIR && rows_used <= C::ROWS / 2 && tb.y - tb.x >= 2 ? 1 : 0) != 0;
+  // Wavefront w runs on SIMD w % 4.  The second half's row blocks are rotated
+  // by a quarter of the workgroup, so that when only one or two row blocks
+  // hold valid rows, their two halves run on different SIMDs rather than
+  // sharing one.
   const int khalf = pair ? wave / (NW / 2) : 0;  // KV half: tiles with index % 2 == khalf
-  const int wrow = pair ? wave % (NW / 2) : wave;  // row block of the tile
+  const int wrow = pair ? (wave + khalf * (NW / 4)) % (NW / 2) : wave;  // row block of the tile
 
   // ---- this lane's query rows, one per row block (both lane halves hold the
   // same rows): tile row wrow*32*RB + 32*rb + col
