@@ -220,16 +220,25 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 // 16-byte asynchronous global->LDS copy: lane i writes lds_base + 16 i.  The
 // compiler does not track these copies; completion is awaited explicitly with
-// vm_wait<>() before the barrier that publishes a stage.
+// vm_wait<>() before the barrier that publishes a stage.  The LDS base goes
+// through M0, which the compiler reserves: the copy saves M0 and puts it back,
+// and leaves one wait state between the M0 write and the copy that reads it.
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(gaddr), "s"(__builtin_amdgcn_readfirstlane(lds_base)) : "memory", "m0");
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+               "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(gaddr), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
 }
 // Same copy from a wave-uniform base plus a 32-bit per-lane byte offset.
 __device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+               "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved)
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
 }
 // Page index of position j: floor(j / page_size) by Granlund-Montgomery
 // multiply-shift (exact for j < 2^24).
