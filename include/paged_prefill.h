@@ -226,6 +226,40 @@ int prefill_attention_tile_bounds_ex(const int32_t* query_start_loc, const int32
                                      int32_t chunk_size, int32_t chunk_lookback,
                                      int32_t* bounds_out, hipStream_t stream);
 
+/*
+ * prefill_attention_check_metadata — checks on the GPU the device-resident preconditions that
+ * prefill_attention states but does not check (a debug aid for callers and tests; the attention
+ * entry points never call it).  It reads query_start_loc [S+1], ctx_lens [S] and, of
+ * block_table [S][max_pages_per_seq], exactly the entries prefill_attention would read (entry p
+ * of sequence s when p * page_size < ctx_lens[s], or < L in cache-sourced mode, cache_only = 1:
+ * the k_new = v_new = NULL mode).  It writes one int32 to the device pointer flags_out: 0 when
+ * every precondition holds, else the OR of
+ *   PAGED_PREFILL_BAD_QSL      query_start_loc[0] != 0, query_start_loc[S] != total_q_tokens, or
+ *                              a decreasing step;
+ *   PAGED_PREFILL_BAD_QLEN     some n_s > max_q_len;
+ *   PAGED_PREFILL_BAD_CTX      some ctx_lens[s] < 0;
+ *   PAGED_PREFILL_BAD_LENGTH   some L = ctx_lens[s] + n_s above 2^24 positions;
+ *   PAGED_PREFILL_BAD_PAGES    some sequence needs more than max_pages_per_seq pages;
+ *   PAGED_PREFILL_BAD_PAGE_ID  a block-table entry that would be read lies outside [0, num_pages).
+ * One workgroup; enqueued on `stream` like the attention call, so the result is valid after the
+ * caller synchronises.  All pointers are device pointers owned by the caller.  Errors:
+ * INVALID_ARG for a null query_start_loc or flags_out, a null ctx_lens with num_seqs > 0, a null
+ * block_table with a non-empty table, page_size <= 0, negative sizes, or cache_only not 0/1;
+ * HIP_ERROR if the launch fails.
+ */
+#define PAGED_PREFILL_BAD_QSL 1
+#define PAGED_PREFILL_BAD_QLEN 2
+#define PAGED_PREFILL_BAD_CTX 4
+#define PAGED_PREFILL_BAD_LENGTH 8
+#define PAGED_PREFILL_BAD_PAGES 16
+#define PAGED_PREFILL_BAD_PAGE_ID 32
+int prefill_attention_check_metadata(const int32_t* block_table,
+                                     const int32_t* query_start_loc, const int32_t* ctx_lens,
+                                     int32_t cache_only, int32_t page_size, int32_t num_seqs,
+                                     int32_t total_q_tokens, int32_t max_q_len,
+                                     int32_t num_pages, int32_t max_pages_per_seq,
+                                     int32_t* flags_out, hipStream_t stream);
+
 /* prefill_attention_strerror — static description of an error code (never NULL). */
 const char* prefill_attention_strerror(int code);
 

@@ -6,11 +6,18 @@ device pointers and streams.
 """
 
 from ._binding import (  # noqa: F401
+    BAD_CTX,
+    BAD_LENGTH,
+    BAD_PAGE_ID,
+    BAD_PAGES,
+    BAD_QLEN,
+    BAD_QSL,
     ERR_HIP,
     ERR_INVALID_ARG,
     ERR_UNSUPPORTED,
     OK,
     PrefillError,
+    check_metadata,
     load_library,
     prefill_attention,
     split_count,

@@ -19,6 +19,14 @@ ERR_INVALID_ARG = -1
 ERR_UNSUPPORTED = -2
 ERR_HIP = -3
 
+# bits of prefill_attention_check_metadata's result
+BAD_QSL = 1
+BAD_QLEN = 2
+BAD_CTX = 4
+BAD_LENGTH = 8
+BAD_PAGES = 16
+BAD_PAGE_ID = 32
+
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
 _F = ctypes.c_float
@@ -36,6 +44,7 @@ _SIGNATURES = {
     "prefill_attention_workspace_size": ([_I] * 4, _U64),
     "prefill_attention_tile_bounds_ex": ([_P, _P] + [_I] * 6 + [_P] + [_I] * 3
                                          + [_P, _I, _I, _I, _P, _P], _I),
+    "prefill_attention_check_metadata": ([_P, _P, _P] + [_I] * 7 + [_P, _P], _I),
 }
 
 _lib = None
@@ -234,6 +243,30 @@ def tile_bounds(query_start_loc, ctx_lens, num_heads: int, num_kv_heads: int, he
     if rc != OK:
         raise PrefillError(rc, "prefill_attention_tile_bounds_ex")
     return out
+
+
+def check_metadata(block_table, query_start_loc, ctx_lens, page_size: int, num_pages: int,
+                   total_q_tokens: int, max_q_len: int, cache_only: bool = False,
+                   stream=None) -> int:
+    """Device-side check of the metadata preconditions of ``prefill_attention``
+    (``prefill_attention_check_metadata``): 0, or the OR of the ``BAD_*`` bits.
+    Synchronises the stream to read the result."""
+    import torch
+    S = int(ctx_lens.shape[0])
+    _check(query_start_loc, "query_start_loc", torch.int32, (S + 1,))
+    _check(ctx_lens, "ctx_lens", torch.int32, (S,))
+    _check(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or int(block_table.shape[0]) != S:
+        raise ValueError("block_table must be [num_seqs, max_pages_per_seq]")
+    flags = torch.full((1,), -1, dtype=torch.int32, device=ctx_lens.device)
+    rc = load_library().prefill_attention_check_metadata(
+        _ptr(block_table), _ptr(query_start_loc), _ptr(ctx_lens), int(bool(cache_only)),
+        int(page_size), S, int(total_q_tokens), int(max_q_len), int(num_pages),
+        int(block_table.shape[1]), _ptr(flags), _stream(stream))
+    if rc != OK:
+        raise PrefillError(rc, "prefill_attention_check_metadata")
+    (torch.cuda.current_stream() if stream is None else stream).synchronize()
+    return int(flags.item())
 
 
 def validate(**kw) -> int:

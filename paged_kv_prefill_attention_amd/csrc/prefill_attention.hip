@@ -1160,6 +1160,48 @@ __global__ void tile_bounds_kernel(const int32_t* qsl, const int32_t* ctx_lens,
   out[2 * idx + 1] = r.y;
 }
 
+// Device-side precondition check (one workgroup): every bit of the result
+// names a precondition of prefill_attention that some sequence breaks.  The
+// block-table entries are visited as a flat (sequence, page) index space so
+// that long tables are shared by all lanes; only the entries the attention
+// kernel would read are examined.
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256)))
+void check_metadata_kernel(const int32_t* block_table, const int32_t* qsl,
+                           const int32_t* ctx_lens, int cache_only, int page_size,
+                           int num_seqs, int total_q_tokens, int max_q_len, int num_pages,
+                           int max_pages_per_seq, int32_t* flags_out) {
+  __shared__ int flags;
+  if (threadIdx.x == 0) flags = 0;
+  __syncthreads();
+  int f = 0;
+  if (threadIdx.x == 0 && (qsl[0] != 0 || qsl[num_seqs] != total_q_tokens))
+    f |= PAGED_PREFILL_BAD_QSL;
+  for (int s = threadIdx.x; s < num_seqs; s += blockDim.x) {
+    const int n = qsl[s + 1] - qsl[s];
+    const int c = ctx_lens[s];
+    if (n < 0) f |= PAGED_PREFILL_BAD_QSL;
+    if (n > max_q_len) f |= PAGED_PREFILL_BAD_QLEN;
+    if (c < 0) f |= PAGED_PREFILL_BAD_CTX;
+    const int64_t L = (int64_t)max(c, 0) + max(n, 0);
+    if (L > kMaxTokens) f |= PAGED_PREFILL_BAD_LENGTH;
+    const int64_t cached = cache_only ? L : max(c, 0);
+    if ((cached + page_size - 1) / page_size > max_pages_per_seq) f |= PAGED_PREFILL_BAD_PAGES;
+  }
+  const int64_t entries = (int64_t)num_seqs * max_pages_per_seq;
+  for (int64_t i = threadIdx.x; i < entries; i += blockDim.x) {
+    const int s = (int)(i / max_pages_per_seq);
+    const int pg = (int)(i - (int64_t)s * max_pages_per_seq);
+    const int64_t L = (int64_t)max(ctx_lens[s], 0) + max(qsl[s + 1] - qsl[s], 0);
+    const int64_t cached = cache_only ? L : max(ctx_lens[s], 0);
+    if ((int64_t)pg * page_size >= cached) continue;  // never read
+    const int id = block_table[i];
+    if (id < 0 || id >= num_pages) f |= PAGED_PREFILL_BAD_PAGE_ID;
+  }
+  if (f != 0) atomicOr(&flags, f);
+  __syncthreads();
+  if (threadIdx.x == 0) *flags_out = flags;
+}
+
 // Split-KV merge (log-sum-exp rule): for each (token, head) row,
 //   out = sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k,  M = max over segments
 // with l_k > 0.  Rows that segment 0 marked with l = -1 belong to an item that
@@ -1464,6 +1506,29 @@ int run_tile_bounds(const int32_t* query_start_loc, const int32_t* ctx_lens, int
   return err == hipSuccess ? PAGED_PREFILL_OK : PAGED_PREFILL_ERR_HIP;
 }
 
+int run_check_metadata(const int32_t* block_table, const int32_t* query_start_loc,
+                       const int32_t* ctx_lens, int32_t cache_only, int32_t page_size,
+                       int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                       int32_t num_pages, int32_t max_pages_per_seq, int32_t* flags_out,
+                       hipStream_t stream) {
+  if (query_start_loc == nullptr || flags_out == nullptr || (cache_only != 0 && cache_only != 1))
+    return PAGED_PREFILL_ERR_INVALID_ARG;
+  if (page_size <= 0 || num_seqs < 0 || total_q_tokens < 0 || max_q_len < 0 || num_pages < 0 ||
+      max_pages_per_seq < 0)
+    return PAGED_PREFILL_ERR_INVALID_ARG;
+  if (num_seqs > 0 && ctx_lens == nullptr) return PAGED_PREFILL_ERR_INVALID_ARG;
+  if ((int64_t)num_seqs * max_pages_per_seq > 0 && block_table == nullptr)
+    return PAGED_PREFILL_ERR_INVALID_ARG;
+  int cm = cache_only, ps = page_size, ns = num_seqs, tq = total_q_tokens, mq = max_q_len,
+      np = num_pages, mp = max_pages_per_seq;
+  void* args[] = {(void*)&block_table, (void*)&query_start_loc, (void*)&ctx_lens, (void*)&cm,
+                  (void*)&ps, (void*)&ns, (void*)&tq, (void*)&mq, (void*)&np, (void*)&mp,
+                  (void*)&flags_out};
+  const hipError_t err = hipLaunchKernel((const void*)&check_metadata_kernel, dim3(1),
+                                         dim3(256), args, 0, stream);
+  return err == hipSuccess ? PAGED_PREFILL_OK : PAGED_PREFILL_ERR_HIP;
+}
+
 Options make_options(const int32_t* causal_per_seq, int32_t mm_clamp, int32_t chunk_size,
                      int32_t chunk_lookback, int32_t kv_splits, void* workspace,
                      uint64_t workspace_bytes) {
@@ -1598,6 +1663,17 @@ int prefill_attention_tile_bounds_ex(const int32_t* query_start_loc, const int32
                          make_options(causal_per_seq, mm_clamp, chunk_size, chunk_lookback, 1,
                                       nullptr, 0),
                          bounds_out, stream);
+}
+
+int prefill_attention_check_metadata(const int32_t* block_table,
+                                     const int32_t* query_start_loc, const int32_t* ctx_lens,
+                                     int32_t cache_only, int32_t page_size, int32_t num_seqs,
+                                     int32_t total_q_tokens, int32_t max_q_len,
+                                     int32_t num_pages, int32_t max_pages_per_seq,
+                                     int32_t* flags_out, hipStream_t stream) {
+  return run_check_metadata(block_table, query_start_loc, ctx_lens, cache_only, page_size,
+                            num_seqs, total_q_tokens, max_q_len, num_pages, max_pages_per_seq,
+                            flags_out, stream);
 }
 
 }  // extern "C"

@@ -146,3 +146,17 @@ def test_split_count_and_workspace_size(lib):
     rows = 3 * 100 * 8
     o_bytes = -(-(rows * 128 * 4) // 256) * 256
     assert ppa.workspace_size(8, 128, 100, 3) == o_bytes + rows * 8
+
+
+def test_check_metadata_rejects_bad_arguments_before_launch(lib):
+    # host checks only: stand-in pointers are never dereferenced
+    import ctypes
+    bt, qsl, ctx, flags = (ctypes.c_void_p(4096 * (i + 1)) for i in range(4))
+    # (block_table, qsl, ctx, cache_only, page_size, S, T, max_q_len, num_pages, max_pages, flags)
+    good = [bt, qsl, ctx, 0, 16, 2, 10, 8, 4, 3, flags]
+    for idx, value in [(1, None), (10, None), (2, None), (0, None), (3, 2), (4, 0), (5, -1),
+                       (6, -1), (7, -1), (8, -1), (9, -1)]:
+        args = list(good)
+        args[idx] = value
+        rc = lib.prefill_attention_check_metadata(*args, None)
+        assert rc == ppa.ERR_INVALID_ARG, (idx, value)
