@@ -748,6 +748,9 @@ void prefill_attention_kernel(const KernelArgs p) {
   // until its first unmasked key; meanwhile its accumulators start at 0.
   constexpr float kLazy = 8.f;
   float m_run[RB], mi[RB], l_run[RB];  // mi = -m_run once the row has one, else 0
+  // A tile's row max (relative to m_run) above thr moves m_run: any key at all
+  // while the row has none (thr = -inf), else a growth beyond 2^kLazy.
+  float thr[RB];
   // Without registers to spare for the splatted start value (D = 256, or two
   // row blocks) the offset is added after the product instead.
   constexpr bool kSplatInit = D <= 128 && RB == 1;
@@ -755,6 +758,7 @@ void prefill_attention_kernel(const KernelArgs p) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     m_run[rb] = -INFINITY;
+    thr[rb] = -INFINITY;
     mi[rb] = 0.f;
     l_run[rb] = 0.f;                   // running row sum (this lane half's keys)
     minit[rb] = f32x16{};
@@ -804,7 +808,8 @@ void prefill_attention_kernel(const KernelArgs p) {
   // fragments of step ks+1 are read before the MFMAs of step ks are issued.
   auto qk = [&](int stage, f32x16 (*sacc)[NKB]) __attribute__((always_inline)) {
     uint32_t kbase = k_lane + (uint32_t)(stage * 2 * TILE_ELEMS * 2);
-    asm volatile("" : "+v"(kbase));  // keep the per-read XORs in the loop (no hoisting)
+    // d = 256 keeps the per-read XORs in the loop (hoisting them spills there)
+    if constexpr (D == 256) asm volatile("" : "+v"(kbase));
     auto kfrag = [&](int kb, int ks) __attribute__((always_inline)) {
       const uint32_t addr = (kbase + (uint32_t)(kb * 32 * D * 2)) ^ (uint32_t)(32 * ks);
       return *(const lds_u32x4*)(uintptr_t)addr;
@@ -876,7 +881,9 @@ void prefill_attention_kernel(const KernelArgs p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) m = fmaxf(m, sacc[rb][kb][r]);
       mx[rb] = pair_max(m);  // row max relative to the reference
-      adj[rb] = m_run[rb] == -INFINITY ? mx[rb] > -INFINITY : mx[rb] > kLazy;
+      // (d = 256 has no register to spare for thr and tests m_run instead)
+      adj[rb] = D <= 128 ? mx[rb] > thr[rb]
+                         : (m_run[rb] == -INFINITY ? mx[rb] > -INFINITY : mx[rb] > kLazy);
       any_adj |= adj[rb];
     }
     if (__builtin_amdgcn_ballot_w64(any_adj) != 0) {  // wave-uniform branch
@@ -897,6 +904,7 @@ void prefill_attention_kernel(const KernelArgs p) {
           for (int r = 0; r < 16; ++r) sacc[rb][kb][r] -= d;
         m_run[rb] = unset ? (adj[rb] ? mx[rb] : m_run[rb]) : m_run[rb] + d;
         mi[rb] = m_run[rb] == -INFINITY ? 0.f : -m_run[rb];
+        thr[rb] = m_run[rb] == -INFINITY ? -INFINITY : kLazy;
         if constexpr (kSplatInit) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) minit[rb][r] = mi[rb];
