@@ -150,8 +150,8 @@ def make_launcher(w, cache_only=False, kv_splits=1):
     import paged_kv_prefill_attention_amd as ppa
     dev = to_device(w, cache_only=cache_only)
     out = torch.empty_like(dev["q"])
-    k = ppa.split_count(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs, w.max_q_len,
-                        kv_splits)
+    k = ppa.split_count(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs,
+                        w.total_q_tokens, w.max_q_len, kv_splits)
     need = ppa.workspace_size(w.num_heads, w.head_size, w.total_q_tokens, k)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
     dev["workspace"] = ws
@@ -258,7 +258,7 @@ def run_suite(path, steps, warmup):
     cases += [(4, None, n) for n in (2048, 4096, 8192, 16384, 32768, 65536)]
     cases = [(cid, P, n, 1) for cid, P, n in cases]
     # split-KV: explicit and automatic counts, beside the unsplit launch
-    cases += [(3, 1040, None, 2), (3, 1040, None, 4)]
+    cases += [(3, 1040, None, 2), (3, 1040, None, 4), (3, 1040, None, 0)]
     cases += [(name, None, None, k) for name in NAMED for k in
               ((1, 0) if name == "long_context_short_chunk" else (1,))]
     for cid, P, n, splits in cases:
@@ -271,7 +271,7 @@ def run_suite(path, steps, warmup):
         flop = useful_flop(w)
         import paged_kv_prefill_attention_amd as ppa
         k = ppa.split_count(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs,
-                            w.max_q_len, splits)
+                            w.total_q_tokens, w.max_q_len, splits)
         rec = {"config": cid, "workload": w.name, "new_tokens": int(w.q_lens.sum()),
                "kv_splits": k, "ms_mean": ms, "ms_median": per[len(per) // 2],
                "ms_device": ms_dev, "device_tflops": flop / (ms_dev / 1e3) / 1e12,

@@ -194,12 +194,16 @@ int prefill_attention_ex(const void* q, const void* k_new, const void* v_new,
 
 /*
  * prefill_attention_kv_splits — the split count prefill_attention_ex uses for kv_splits
- * (kv_splits itself when > 0; for 0, 1 when the batch has at least 512 Q-tile work items,
- * else enough segments for about 512 workgroups, at most 16).  Host-only.  Returns the count
- * (>= 1) or a negative error code (INVALID_ARG, UNSUPPORTED as for tile_config).
+ * (kv_splits itself when > 0; for 0, 1 when the batch may have at least 512 Q-tile work
+ * items, else enough segments for about 512 workgroups, at most 16).  The item count is
+ * bounded from the sizes alone: at most num_seqs * cdiv(max_q_len, block_q) Q tiles, and at
+ * most (total_q_tokens + num_seqs * (block_q - 1)) / block_q.  Host-only.  Returns the count
+ * (>= 1) or a negative error code (INVALID_ARG for negative sizes or kv_splits outside
+ * [0, 64]; UNSUPPORTED as for tile_config).
  */
 int prefill_attention_kv_splits(int32_t head_size, int32_t num_heads, int32_t num_kv_heads,
-                                int32_t num_seqs, int32_t max_q_len, int32_t kv_splits);
+                                int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                                int32_t kv_splits);
 
 /*
  * prefill_attention_workspace_size — bytes of workspace prefill_attention_ex needs with

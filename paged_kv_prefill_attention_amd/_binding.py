@@ -40,7 +40,7 @@ _SIGNATURES = {
     "prefill_attention_strerror": ([_I], ctypes.c_char_p),
     "prefill_attention_ex": ([_P] * 8 + [_I] * 7 + [_P, _F, _P] + [_I] * 6
                              + [_P, _I, _I, _I, _I, _P, _U64, _P], _I),
-    "prefill_attention_kv_splits": ([_I] * 6, _I),
+    "prefill_attention_kv_splits": ([_I] * 7, _I),
     "prefill_attention_workspace_size": ([_I] * 4, _U64),
     "prefill_attention_tile_bounds_ex": ([_P, _P] + [_I] * 6 + [_P] + [_I] * 3
                                          + [_P, _I, _I, _I, _P, _P], _I),
@@ -123,10 +123,11 @@ def _stream(stream):
 
 
 def split_count(head_size: int, num_heads: int, num_kv_heads: int, num_seqs: int,
-                max_q_len: int, requested: int = 0) -> int:
+                total_q_tokens: int, max_q_len: int, requested: int = 0) -> int:
     """The split-KV segment count the library uses for ``requested`` (0 = automatic)."""
     rc = load_library().prefill_attention_kv_splits(head_size, num_heads, num_kv_heads,
-                                                    num_seqs, max_q_len, requested)
+                                                    num_seqs, total_q_tokens, max_q_len,
+                                                    requested)
     if rc < 0:
         raise PrefillError(rc, "prefill_attention_kv_splits")
     return rc
@@ -198,7 +199,7 @@ def prefill_attention(q, k_new, v_new, k_cache, v_cache, block_table, query_star
         return out
     if causal_per_seq is not None:
         _check(causal_per_seq, "causal_per_seq", torch.int32, (S,))
-    splits = split_count(d, H, Hkv, S, int(max_q_len), int(kv_splits))
+    splits = split_count(d, H, Hkv, S, T, int(max_q_len), int(kv_splits))
     need = workspace_size(H, d, T, splits)
     if need > 0:
         if workspace is None:

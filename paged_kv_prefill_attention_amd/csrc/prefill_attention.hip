@@ -1365,10 +1365,15 @@ int64_t item_slots(int num_seqs, int num_kv_heads, int64_t num_q_tiles, int head
 
 // Split count for kv_splits (0 = automatic): split only when the batch has
 // fewer Q-tile work items than twice the 256 CUs, to about 512 workgroups.
+// The Q tiles of the batch number at most num_seqs * cdiv(max_q_len, block_q)
+// and at most sum over s of cdiv(n_s, block_q) <= (T + S (block_q - 1)) / block_q.
 int resolve_splits(int kv_splits, int num_seqs, int num_kv_heads, int head_blocks,
-                   int64_t num_q_tiles) {
+                   int64_t num_q_tiles, int total_q_tokens, int block_q) {
   if (kv_splits > 0) return kv_splits;
-  const int64_t items = (int64_t)num_seqs * num_kv_heads * head_blocks * num_q_tiles;
+  const int64_t tiles = std::min<int64_t>(
+      (int64_t)num_seqs * num_q_tiles,
+      ((int64_t)total_q_tokens + (int64_t)num_seqs * (block_q - 1)) / block_q);
+  const int64_t items = tiles * num_kv_heads * head_blocks;
   if (items >= 512 || items <= 0) return 1;
   return (int)std::min<int64_t>(16, (512 + items - 1) / items);
 }
@@ -1456,7 +1461,7 @@ int run(const void* q, const void* k_new, const void* v_new, const void* k_cache
   const int64_t num_q_tiles = ((int64_t)max_q_len + tc.block_q - 1) / tc.block_q;
   a.num_q_tiles = (int32_t)num_q_tiles;
   const int splits = resolve_splits(o.kv_splits, num_seqs, num_kv_heads, a.head_blocks,
-                                    num_q_tiles);
+                                    num_q_tiles, total_q_tokens, tc.block_q);
   a.kv_splits = splits;
   a.part_o = nullptr;
   a.part_ml = nullptr;
@@ -1628,15 +1633,18 @@ int prefill_attention_ex(const void* q, const void* k_new, const void* v_new,
 }
 
 int prefill_attention_kv_splits(int32_t head_size, int32_t num_heads, int32_t num_kv_heads,
-                                int32_t num_seqs, int32_t max_q_len, int32_t kv_splits) {
-  if (kv_splits < 0 || kv_splits > kMaxSplits || num_seqs < 0 || max_q_len < 0)
+                                int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                                int32_t kv_splits) {
+  if (kv_splits < 0 || kv_splits > kMaxSplits || num_seqs < 0 || total_q_tokens < 0 ||
+      max_q_len < 0)
     return PAGED_PREFILL_ERR_INVALID_ARG;
   TileChoice tc;
   const int rc = choose_tiles(head_size, num_heads, num_kv_heads, &tc);
   if (rc != PAGED_PREFILL_OK) return rc;
   const int64_t num_q_tiles = ((int64_t)max_q_len + tc.block_q - 1) / tc.block_q;
   return resolve_splits(kv_splits, num_seqs, num_kv_heads,
-                        num_heads / num_kv_heads / tc.heads_per_tile, num_q_tiles);
+                        num_heads / num_kv_heads / tc.heads_per_tile, num_q_tiles,
+                        total_q_tokens, tc.block_q);
 }
 
 uint64_t prefill_attention_workspace_size(int32_t num_heads, int32_t head_size,

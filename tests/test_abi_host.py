@@ -135,13 +135,19 @@ def test_invalid_ex_options_return_before_launch(lib):
 
 def test_split_count_and_workspace_size(lib):
     # explicit counts pass through; automatic splits only small batches
-    assert ppa.split_count(128, 64, 64, 8, 873, 1) == 1
-    assert ppa.split_count(128, 64, 64, 8, 873, 5) == 5
-    assert ppa.split_count(128, 64, 64, 8, 873, 0) == 1        # 8*64*4 = 2048 items
-    assert ppa.split_count(128, 32, 8, 2, 256, 0) == 8         # 2*8*4 = 64 items -> 512/64
-    assert ppa.split_count(64, 8, 8, 1, 64, 0) == 16           # 8 items, capped at 16
+    assert ppa.split_count(128, 64, 64, 8, 3317, 873, 1) == 1
+    assert ppa.split_count(128, 64, 64, 8, 3317, 873, 5) == 5
+    assert ppa.split_count(128, 64, 64, 8, 3317, 873, 0) == 1   # <= 20 Q tiles x 64 heads
+    assert ppa.split_count(128, 32, 8, 2, 456, 256, 0) == 8     # 2*4 tiles x 8 = 64 items
+    assert ppa.split_count(64, 8, 8, 1, 64, 64, 0) == 16        # 8 items, capped at 16
+    # the 8-sequence d=256 GQA batch: max_q_len alone allows 8*32 tiles x 2 KV heads = 512
+    # items, but 10155 tokens allow at most (10155 + 8*63) / 64 = 166 tiles -> 332 items
+    assert ppa.split_count(256, 8, 2, 8, 10155, 2048, 0) == 2
+    assert ppa.split_count(256, 8, 2, 8, 1 << 20, 2048, 0) == 1
     with pytest.raises(ppa.PrefillError):
-        ppa.split_count(128, 8, 8, 1, 64, 65)
+        ppa.split_count(128, 8, 8, 1, 64, 64, 65)
+    with pytest.raises(ppa.PrefillError):
+        ppa.split_count(128, 8, 8, 1, -1, 64, 0)
     assert ppa.workspace_size(8, 128, 100, 1) == 0
     rows = 3 * 100 * 8
     o_bytes = -(-(rows * 128 * 4) // 256) * 256

@@ -65,6 +65,19 @@ def test_full_size_configs_sampled(cid, P):
     print("%s max_abs=%.3g max_rel=%.3g" % (w.name, err[0], err[1]), flush=True)
 
 
+def test_config3_automatic_split_sampled():
+    """The d=256 GQA batch under the automatic split count (two segments: its token count
+    bounds it to 332 Q-tile items), in the launch configuration the suite times."""
+    import paged_kv_prefill_attention_amd as ppa
+    w = make_config(3, page_size=1040)
+    k = ppa.split_count(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs,
+                        w.total_q_tokens, w.max_q_len, 0)
+    assert k == 2
+    out = out_to_f32(run_gpu(w, kv_splits=0))
+    err = check_sampled(w, out, seed=33)
+    print("%s auto split max_abs=%.3g max_rel=%.3g" % (w.name, err[0], err[1]), flush=True)
+
+
 def test_config3_page_sizes_bitwise_equal():
     """Tiles never depend on pages: 1040 and 1056 give the same bits."""
     import torch

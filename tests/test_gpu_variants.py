@@ -114,7 +114,8 @@ def test_split_kv_long_context_short_chunk():
     w = make_workload(seed=515, ctx_lens=[32768, 30000], q_lens=[256, 200], num_heads=32,
                       num_kv_heads=8, head_size=128, page_size=16, causal=True,
                       name="long_ctx_short_chunk")
-    k = ppa.split_count(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs, w.max_q_len, 0)
+    k = ppa.split_count(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs,
+                        w.total_q_tokens, w.max_q_len, 0)
     assert k > 1
     out = out_to_f32(run_gpu(w, kv_splits=0))
     bq, _ = ppa.tile_config(w.head_size, w.num_heads, w.num_kv_heads)
