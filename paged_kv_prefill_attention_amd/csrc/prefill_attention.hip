@@ -1350,11 +1350,17 @@ void page_magic(int page_size, uint32_t* magic, int* shift) {
 }
 
 // Workgroups per split before the split factor: 8 XCDs x slots per XCD.
-int64_t item_slots(int num_seqs, int num_kv_heads, int64_t num_q_tiles, int head_blocks) {
+int64_t item_slots(int num_seqs, int num_kv_heads, int64_t num_q_tiles, int head_blocks,
+                   int total_q_tokens, int block_q) {
   if (num_seqs <= kSortMaxSeqs) {
     // items dealt round-robin over the XCDs: at most one per (sequence, KV
-    // head, Q tile, head block), rounded up to whole rounds
-    const int64_t items = (int64_t)num_seqs * num_kv_heads * num_q_tiles * head_blocks;
+    // head, Q tile, head block), rounded up to whole rounds.  The Q tiles are
+    // at most S * cdiv(max_q_len, block_q) and at most (T + S (block_q - 1)) /
+    // block_q; slots past the batch's items exit at once.
+    const int64_t tiles = std::min<int64_t>(
+        (int64_t)num_seqs * num_q_tiles,
+        ((int64_t)total_q_tokens + (int64_t)num_seqs * (block_q - 1)) / block_q);
+    const int64_t items = tiles * num_kv_heads * head_blocks;
     return (items + kNumXcd - 1) / kNumXcd * kNumXcd;
   }
   // large batches: per XCD a contiguous range of (sequence, KV head) groups,
@@ -1473,7 +1479,9 @@ int run(const void* q, const void* k_new, const void* v_new, const void* k_cache
     a.part_o = (float*)o.workspace;
     a.part_ml = (float2*)((char*)o.workspace + o_bytes);
   }
-  const int64_t grid = item_slots(num_seqs, num_kv_heads, num_q_tiles, a.head_blocks) * splits;
+  const int64_t grid =
+      item_slots(num_seqs, num_kv_heads, num_q_tiles, a.head_blocks, total_q_tokens,
+                 tc.block_q) * splits;
   if (grid > 0x7fffffff) return PAGED_PREFILL_ERR_UNSUPPORTED;
   hipError_t err;
   switch (head_size) {
