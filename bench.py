@@ -273,7 +273,8 @@ def run_suite(path, steps, warmup):
         k = ppa.split_count(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs,
                             w.total_q_tokens, w.max_q_len, splits)
         rec = {"config": cid, "workload": w.name, "new_tokens": int(w.q_lens.sum()),
-               "kv_splits": k, "ms_mean": ms, "ms_median": per[len(per) // 2],
+               "kv_splits": k, "requested_splits": splits, "ms_mean": ms,
+               "ms_median": per[len(per) // 2],
                "ms_device": ms_dev, "device_tflops": flop / (ms_dev / 1e3) / 1e12,
                "useful_tflops": flop / (ms / 1e3) / 1e12,
                "frac_mfma_peak": flop / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
