@@ -258,7 +258,7 @@ def run_suite(path, steps, warmup):
     cases += [(4, None, n) for n in (2048, 4096, 8192, 16384, 32768, 65536)]
     cases = [(cid, P, n, 1) for cid, P, n in cases]
     # split-KV: explicit and automatic counts, beside the unsplit launch
-    cases += [(3, 1040, None, 2), (3, 1040, None, 4), (3, 1040, None, 0)]
+    cases += [(3, 1040, None, 2), (3, 1040, None, 4), (3, 1040, None, 0), (5, None, None, 0)]
     cases += [(name, None, None, k) for name in NAMED for k in
               ((1, 0) if name == "long_context_short_chunk" else (1,))]
     for cid, P, n, splits in cases:

@@ -193,11 +193,19 @@ int prefill_attention_ex(const void* q, const void* k_new, const void* v_new,
                          uint64_t workspace_bytes, hipStream_t stream);
 
 /*
- * prefill_attention_kv_splits — the split count prefill_attention_ex uses for kv_splits
- * (kv_splits itself when > 0; for 0, 1 when the batch may have at least 512 Q-tile work
- * items, else enough segments for about 512 workgroups, at most 16).  The item count is
- * bounded from the sizes alone: at most num_seqs * cdiv(max_q_len, block_q) Q tiles, and at
- * most (total_q_tokens + num_seqs * (block_q - 1)) / block_q.  Host-only.  Returns the count
+ * prefill_attention_kv_splits — the split count prefill_attention_ex uses for kv_splits,
+ * and so the workspace it needs.  kv_splits > 0: kv_splits itself.  kv_splits = 0
+ * (automatic), with W the workgroups the GPU runs at once (CUs times the workgroups of this
+ * head size that one CU holds: 256 or 512 on MI355X) and the Q-tile work items bounded from
+ * the sizes alone (at most num_seqs * cdiv(max_q_len, block_q) Q tiles, and at most
+ * (total_q_tokens + num_seqs * (block_q - 1)) / block_q, times the KV heads):
+ *   - fewer than 2W items: enough segments for about 2W workgroups, at most 16; every item
+ *     longer than its share is cut;
+ *   - 2W to 4W items whose last round is at most a quarter full (num_seqs <= 256): 4, and
+ *     only the items of that last round are cut, by workgroups appended to the grid (the
+ *     kernel counts those items exactly from the device-side lengths);
+ *   - otherwise 1.
+ * Host-only (it asks the runtime for the current device's CU count).  Returns the count
  * (>= 1) or a negative error code (INVALID_ARG for negative sizes or kv_splits outside
  * [0, 64]; UNSUPPORTED as for tile_config).
  */

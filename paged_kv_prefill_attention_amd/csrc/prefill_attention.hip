@@ -114,6 +114,12 @@ struct KernelArgs {
   int32_t total_q_tokens;
   float* part_o;           // [kv_splits][T][H][d] unnormalised partial O (kv_splits > 1)
   float2* part_ml;         // [kv_splits][T][H] (m, l) of each partial, log2 units
+  // Tail splitting (kv_splits segments for the items of the last partial round
+  // only): main_slots item slots, then helper slots; round_slots workgroups
+  // run at once.  tail_mode = 0: the segment-cap rule above applies instead.
+  int32_t tail_mode;
+  int32_t main_slots;
+  int32_t round_slots;
 };
 
 // ---------------------------------------------------------------------------
@@ -302,6 +308,8 @@ struct TileLayout {
 struct WorkItem {
   int s, g, hblk, t;
   bool valid;
+  bool split;  // tail splitting: this item is cut into kv_splits segments
+  int piece;   // the segment this slot computes
 };
 
 __device__ __forceinline__ int seq_ntiles(const int32_t* qsl, int s, int block_q) {
@@ -327,7 +335,7 @@ __device__ WorkItem decode_work(const Args& p, int b, int tid, int nthreads, Seq
   const int HBLK = p.head_blocks;
   const int x = b % kNumXcd;
   int k = b / kNumXcd;
-  WorkItem w{0, 0, 0, 0, false};
+  WorkItem w{0, 0, 0, 0, false, false, 0};
   if (S <= kSortMaxSeqs) {
     for (int i = tid; i < S; i += nthreads) {
       const int a = p.qsl[i], e = p.qsl[i + 1], cl = p.ctx_lens[i];
@@ -353,6 +361,27 @@ __device__ WorkItem decode_work(const Args& p, int b, int tid, int nthreads, Seq
     // Consecutive items of one Q tile are equal work, which suits the strict
     // rotation in which an XCD hands its workgroups to its shader engines.
     int j = k * kNumXcd + x;
+    if (p.tail_mode) {
+      // Tail splitting.  The items past the last whole round (total mod
+      // round_slots of them, the lightest) would run alone at the end; when
+      // they fill at most a quarter of a round, the last m of them are cut
+      // into kv_splits segments: segment 0 in the item's own slot, the others
+      // in the helper slots that follow the main ones.
+      int total = 0;
+      for (int sr = 0; sr < S; ++sr) total += ntiles_by_rank[sr];
+      total *= Hkv * HBLK;
+      const int ks = p.kv_splits;
+      const int helpers = (int)gridDim.x - p.main_slots;
+      const int tail = total % p.round_slots;
+      const int m = tail <= p.round_slots / 4 ? min(tail, helpers / (ks - 1)) : 0;
+      if (j >= p.main_slots) {  // helper slot: segment 1 + h % (ks - 1) of tail item h / (ks - 1)
+        const int h = j - p.main_slots;
+        if (h / (ks - 1) >= m) return w;
+        w.piece = 1 + h % (ks - 1);
+        j = total - m + h / (ks - 1);
+      }
+      w.split = j >= total - m && j < total;
+    }
     for (int sr = 0; sr < S; ++sr) {
       const int per_tile = Hkv * HBLK;
       const int per_seq = per_tile * ntiles_by_rank[sr];
@@ -412,6 +441,12 @@ struct TileShape {
   static constexpr bool PAIR = NW % 2 == 0 && NW / 2 * 64 * XREGS * 4 <= LDS_BYTES;
   // The output tile (ROWS x D bf16) is staged through the ring for row-wise stores.
   static constexpr bool STAGE_OUT = ROWS * D * 2 <= LDS_BYTES;
+  // Workgroups resident per CU: four SIMDs of WPE wavefronts, 160 KiB of LDS
+  // (ring, block-table cache, sequence table and a little slack).
+  static constexpr int LDS_TOTAL = LDS_BYTES + BT_CACHE * 4 + 6 * 1024;
+  static constexpr int WG_PER_CU = (4 * WPE / NW) < (160 * 1024 / LDS_TOTAL)
+                                       ? (4 * WPE / NW) : (160 * 1024 / LDS_TOTAL);
+  static_assert(WG_PER_CU >= 1, "a workgroup must fit a CU");
   static_assert(DMA_PER_TENSOR % NW == 0, "copies must split evenly over the wavefronts");
   static_assert(BN % 32 == 0 && D % 32 == 0, "MFMA blocking");
   static_assert(NSTAGE >= 2 && NSTAGE <= 6, "ring depth");
@@ -451,14 +486,16 @@ void prefill_attention_kernel(const KernelArgs p) {
   // the hardware hands an XCD's workgroups to its 4 shader engines in strict
   // rotation, so the segment-0 slot is placed per item such that those slots
   // fall on every engine in turn.
-  const int ks = p.kv_splits;
+  // Under tail splitting every slot is one item (or a helper segment), and
+  // decode_work says which segment.
+  const int ks = p.tail_mode ? 1 : p.kv_splits;
   const int pos = (int)((blockIdx.x / kNumXcd) % ks);
   const int item_idx = (int)((blockIdx.x / kNumXcd) / ks);
   const int pos0 = ks % 2 ? 0 : (ks % 4 == 2 ? (item_idx / 2) % 2 : item_idx % 4);
-  const int split = (pos + ks - pos0) % ks;
-  const int bitem = (int)((blockIdx.x / kNumXcd) / p.kv_splits) * kNumXcd + blockIdx.x % kNumXcd;
+  const int bitem = (int)((blockIdx.x / kNumXcd) / ks) * kNumXcd + blockIdx.x % kNumXcd;
   const WorkItem wi = decode_work(p, bitem, tid, C::THREADS, seqs);
   if (!wi.valid) return;  // padding slot
+  const int split = p.tail_mode ? wi.piece : (pos + ks - pos0) % ks;
   const int s = wi.s;
   const int g = wi.g;
   const int hblk = wi.hblk;
@@ -485,7 +522,15 @@ void prefill_attention_kernel(const KernelArgs p) {
   // cap = ceil(tiles of the longest sequence / kv_splits), so only the items
   // that would hold back the tail are split and pay for partial results.
   bool whole = true;
-  if (p.kv_splits > 1) {
+  if (p.tail_mode) {
+    if (wi.split) {  // segment `split` of kv_splits equal runs (possibly empty)
+      const int k = p.kv_splits;
+      const int per = (tb.y - tb.x + k - 1) / k;
+      const int x0 = min(tb.x + split * per, tb.y);
+      tb = make_int2(x0, min(x0 + per, tb.y));
+      whole = false;
+    }
+  } else if (p.kv_splits > 1) {
     const int k = p.kv_splits;
     const int n_item = tb.y - tb.x;
     const int lmax = staged ? seqs.key[seqs.order[0]] : 0;  // heaviest sequence first
@@ -1258,6 +1303,7 @@ struct TileChoice {
   int block_n;
   int heads_per_tile;
   int block_q;
+  int wg_per_cu;  // workgroups resident per CU
 };
 
 int gcd_int(int a, int b) {
@@ -1270,9 +1316,10 @@ int gcd_int(int a, int b) {
 }
 
 // Query rows and keys per KV tile of the shape compiled for a head size.
-template <int D> void shape_of(int* rows, int* bn) {
+template <int D> void shape_of(int* rows, int* bn, int* wgs) {
   *rows = ShapeFor<D>::T::ROWS;
   *bn = ShapeFor<D>::T::BN;
+  *wgs = ShapeFor<D>::T::WG_PER_CU;
 }
 
 int choose_tiles(int head_size, int num_heads, int num_kv_heads, TileChoice* tc) {
@@ -1280,15 +1327,16 @@ int choose_tiles(int head_size, int num_heads, int num_kv_heads, TileChoice* tc)
     return PAGED_PREFILL_ERR_INVALID_ARG;
   if (head_size != 64 && head_size != 128 && head_size != 256)
     return PAGED_PREFILL_ERR_UNSUPPORTED;
-  int rows, bn;
-  if (head_size == 64) shape_of<64>(&rows, &bn);
-  else if (head_size == 128) shape_of<128>(&rows, &bn);
-  else shape_of<256>(&rows, &bn);
+  int rows, bn, wgs;
+  if (head_size == 64) shape_of<64>(&rows, &bn, &wgs);
+  else if (head_size == 128) shape_of<128>(&rows, &bn, &wgs);
+  else shape_of<256>(&rows, &bn, &wgs);
   const int group = num_heads / num_kv_heads;
   const int hpt = gcd_int(group, rows);  // heads of one group that share a tile
   tc->block_n = bn;
   tc->heads_per_tile = hpt;
   tc->block_q = rows / hpt;
+  tc->wg_per_cu = wgs;
   return PAGED_PREFILL_OK;
 }
 
@@ -1369,19 +1417,49 @@ int64_t item_slots(int num_seqs, int num_kv_heads, int64_t num_q_tiles, int head
   return kNumXcd * groups_per_xcd * num_q_tiles * head_blocks;
 }
 
-// Split count for kv_splits (0 = automatic): split only when the batch has
-// fewer Q-tile work items than twice the 256 CUs, to about 512 workgroups.
-// The Q tiles of the batch number at most num_seqs * cdiv(max_q_len, block_q)
-// and at most sum over s of cdiv(n_s, block_q) <= (T + S (block_q - 1)) / block_q.
-int resolve_splits(int kv_splits, int num_seqs, int num_kv_heads, int head_blocks,
-                   int64_t num_q_tiles, int total_q_tokens, int block_q) {
-  if (kv_splits > 0) return kv_splits;
+// Split count for kv_splits (0 = automatic).  The Q tiles of the batch number
+// at most num_seqs * cdiv(max_q_len, block_q) and at most sum over s of
+// cdiv(n_s, block_q) <= (T + S (block_q - 1)) / block_q; times the KV heads and
+// head blocks, that bounds the work items.  Automatic choice:
+//  - fewer than twice round_slots items: split every long item (the segment-cap
+//    rule), to about 2 * round_slots workgroups, at most 16 segments;
+//  - two to four rounds of items whose bound leaves a last round at most a
+//    quarter full, for batches whose items the kernel ranks (num_seqs <=
+//    kSortMaxSeqs): tail splitting with kTailSplits segments, which cuts only
+//    the items of that short last round (the kernel counts them exactly);
+//  - otherwise no split.
+constexpr int kTailSplits = 4;
+struct SplitChoice {
+  int splits;
+  int tail;  // 1: tail splitting
+};
+SplitChoice choose_splits(int kv_splits, int num_seqs, int num_kv_heads, int head_blocks,
+                          int64_t num_q_tiles, int total_q_tokens, int block_q,
+                          int round_slots) {
+  if (kv_splits > 0) return {kv_splits, 0};
   const int64_t tiles = std::min<int64_t>(
       (int64_t)num_seqs * num_q_tiles,
       ((int64_t)total_q_tokens + (int64_t)num_seqs * (block_q - 1)) / block_q);
   const int64_t items = tiles * num_kv_heads * head_blocks;
-  if (items >= 512 || items <= 0) return 1;
-  return (int)std::min<int64_t>(16, (512 + items - 1) / items);
+  if (items <= 0) return {1, 0};
+  if (items < 2 * (int64_t)round_slots)
+    return {(int)std::min<int64_t>(16, (2 * (int64_t)round_slots + items - 1) / items), 0};
+  const int64_t tail = items % round_slots;
+  if (num_seqs <= kSortMaxSeqs && items <= 4 * (int64_t)round_slots && tail > 0 &&
+      tail <= round_slots / 4)
+    return {kTailSplits, 1};
+  return {1, 0};
+}
+
+// Workgroups that run at once: CUs of the current device times the workgroups
+// one CU holds.
+int round_slots_for(const TileChoice& tc) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;  // MI355X
+  return cus * tc.wg_per_cu;
 }
 
 uint64_t workspace_bytes_for(int num_heads, int head_size, int total_q_tokens, int splits) {
@@ -1466,9 +1544,13 @@ int run(const void* q, const void* k_new, const void* v_new, const void* k_cache
 
   const int64_t num_q_tiles = ((int64_t)max_q_len + tc.block_q - 1) / tc.block_q;
   a.num_q_tiles = (int32_t)num_q_tiles;
-  const int splits = resolve_splits(o.kv_splits, num_seqs, num_kv_heads, a.head_blocks,
-                                    num_q_tiles, total_q_tokens, tc.block_q);
+  const int round_slots = round_slots_for(tc);
+  const SplitChoice sc = choose_splits(o.kv_splits, num_seqs, num_kv_heads, a.head_blocks,
+                                       num_q_tiles, total_q_tokens, tc.block_q, round_slots);
+  const int splits = sc.splits;
   a.kv_splits = splits;
+  a.tail_mode = sc.tail;
+  a.round_slots = round_slots;
   a.part_o = nullptr;
   a.part_ml = nullptr;
   if (splits > 1) {
@@ -1479,10 +1561,12 @@ int run(const void* q, const void* k_new, const void* v_new, const void* k_cache
     a.part_o = (float*)o.workspace;
     a.part_ml = (float2*)((char*)o.workspace + o_bytes);
   }
-  const int64_t grid =
-      item_slots(num_seqs, num_kv_heads, num_q_tiles, a.head_blocks, total_q_tokens,
-                 tc.block_q) * splits;
+  const int64_t main_slots = item_slots(num_seqs, num_kv_heads, num_q_tiles, a.head_blocks,
+                                        total_q_tokens, tc.block_q);
+  // tail splitting: one slot per item, then one round of helper slots
+  const int64_t grid = sc.tail ? main_slots + round_slots : main_slots * splits;
   if (grid > 0x7fffffff) return PAGED_PREFILL_ERR_UNSUPPORTED;
+  a.main_slots = (int32_t)main_slots;
   hipError_t err;
   switch (head_size) {
     case 64: err = launch<64>(a, (uint32_t)grid, stream); break;
@@ -1650,9 +1734,9 @@ int prefill_attention_kv_splits(int32_t head_size, int32_t num_heads, int32_t nu
   const int rc = choose_tiles(head_size, num_heads, num_kv_heads, &tc);
   if (rc != PAGED_PREFILL_OK) return rc;
   const int64_t num_q_tiles = ((int64_t)max_q_len + tc.block_q - 1) / tc.block_q;
-  return resolve_splits(kv_splits, num_seqs, num_kv_heads,
-                        num_heads / num_kv_heads / tc.heads_per_tile, num_q_tiles,
-                        total_q_tokens, tc.block_q);
+  return choose_splits(kv_splits, num_seqs, num_kv_heads,
+                       num_heads / num_kv_heads / tc.heads_per_tile, num_q_tiles,
+                       total_q_tokens, tc.block_q, round_slots_for(tc)).splits;
 }
 
 uint64_t prefill_attention_workspace_size(int32_t num_heads, int32_t head_size,

@@ -143,7 +143,13 @@ def test_split_count_and_workspace_size(lib):
     # the 8-sequence d=256 GQA batch: max_q_len alone allows 8*32 tiles x 2 KV heads = 512
     # items, but 10155 tokens allow at most (10155 + 8*63) / 64 = 166 tiles -> 332 items
     assert ppa.split_count(256, 8, 2, 8, 10155, 2048, 0) == 2
-    assert ppa.split_count(256, 8, 2, 8, 1 << 20, 2048, 0) == 1
+    # two to four rounds of items with a last round at most a quarter full: tail splitting
+    assert ppa.split_count(256, 16, 8, 1, 12454, 12454, 0) == 4   # 784 items, 16 past 3 rounds
+    assert ppa.split_count(64, 8, 8, 1, 16640, 16640, 0) == 4     # 1040 items, 512 per round
+    assert ppa.split_count(64, 8, 8, 1, 16384, 16384, 0) == 1     # 1024 items: whole rounds
+    assert ppa.split_count(256, 8, 2, 8, 1 << 20, 2048, 0) == 1   # 512 items: whole rounds
+    assert ppa.split_count(128, 8, 8, 1, 256 * 80, 256 * 80, 0) == 1  # tail of 128: too full
+    assert ppa.split_count(128, 64, 64, 8, 1 << 20, 1024, 0) == 1  # 2048 items: no split
     with pytest.raises(ppa.PrefillError):
         ppa.split_count(128, 8, 8, 1, 64, 64, 65)
     with pytest.raises(ppa.PrefillError):

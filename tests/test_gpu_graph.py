@@ -35,7 +35,7 @@ def launcher(w, dev, out, kv_splits, workspace):
     return fn
 
 
-@pytest.mark.parametrize("case,kv_splits", [(2, 1), (5, 1), (3, 2), (3, 0),
+@pytest.mark.parametrize("case,kv_splits", [(2, 1), (5, 1), (5, 0), (3, 2), (3, 0),
                                             ("long_context_short_chunk", 0),
                                             ("window_mm_prefix_unclamped", 1)])
 def test_graph_replays_match_eager_bitwise(case, kv_splits):

@@ -210,3 +210,42 @@ def test_short_last_tiles_split_kv_tiles_between_halves(d, heads, splits):
         print(describe(w), "splits", splits, flush=True)
         compare(out_to_f32(run_gpu(w, kv_splits=splits)), oracle_full(w),
                 "%s splits=%d" % (w.name, splits))
+
+
+@pytest.mark.parametrize("d,n,causal,wl,wr,note", [
+    (128, 256 * 66, True, 511, -1, "528 items: last 16 split"),
+    (64, 128 * 130, False, 64, 64, "1040 items, two workgroups per CU: last 16 split"),
+])
+def test_tail_splitting_automatic(d, n, causal, wl, wr, note):
+    """Automatic split count on batches of two to four rounds of items: the kernel cuts
+    only the items of a short last round (the first Q tiles of the sequence, since the
+    last Q tile goes first) into segments run by helper slots, merged by log-sum-exp.
+    Every row of those first Q tiles is checked, plus sampled rows elsewhere."""
+    import paged_kv_prefill_attention_amd as ppa
+    w = make_workload(seed=7100 + d + n % 97, ctx_lens=[0], q_lens=[n], num_heads=8,
+                      num_kv_heads=8, head_size=d, page_size=16, causal=causal,
+                      window_left=wl, window_right=wr, name="tail_%d_%d" % (d, n))
+    print(w.name, note, flush=True)
+    assert ppa.split_count(d, 8, 8, 1, n, n, 0) == 4
+    out = out_to_f32(run_gpu(w, kv_splits=0))
+    bq, _ = ppa.tile_config(d, 8, 8)
+    first = np.arange(0, 2 * bq)
+    compare(out[first], oracle_rows(w, 0, first), "%s first Q tiles" % w.name)
+    rows = sample_rows(n, bq, np.random.default_rng(d), extra=24)
+    compare(out[rows], oracle_rows(w, 0, rows), "%s sampled rows" % w.name)
+
+
+def test_tail_splitting_config5():
+    """The window-clamped multimodal prefix workload (784 items of near-equal length) in
+    the automatic mode: its last 16 items, Q tiles 0 and 1 of every KV head, are split."""
+    import paged_kv_prefill_attention_amd as ppa
+    from workloads import make_config
+    w = make_config(5)
+    assert ppa.split_count(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs,
+                           w.total_q_tokens, w.max_q_len, 0) == 4
+    out = out_to_f32(run_gpu(w, kv_splits=0))
+    bq, _ = ppa.tile_config(w.head_size, w.num_heads, w.num_kv_heads)
+    first = np.arange(0, 2 * bq)
+    compare(out[first], oracle_rows(w, 0, first), "config 5 first Q tiles")
+    rows = sample_rows(int(w.q_lens[0]), bq, np.random.default_rng(5), extra=24)
+    compare(out[rows], oracle_rows(w, 0, rows), "config 5 sampled rows")
