@@ -1436,7 +1436,7 @@ struct SplitChoice {
 SplitChoice choose_splits(int kv_splits, int num_seqs, int num_kv_heads, int head_blocks,
                           int64_t num_q_tiles, int total_q_tokens, int block_q,
                           int round_slots) {
-  if (kv_splits > 0) return {kv_splits, 0};
+  if (kv_splits > 0 || round_slots <= 0) return {kv_splits > 0 ? kv_splits : 1, 0};
   const int64_t tiles = std::min<int64_t>(
       (int64_t)num_seqs * num_q_tiles,
       ((int64_t)total_q_tokens + (int64_t)num_seqs * (block_q - 1)) / block_q);
@@ -1544,7 +1544,8 @@ int run(const void* q, const void* k_new, const void* v_new, const void* k_cache
 
   const int64_t num_q_tiles = ((int64_t)max_q_len + tc.block_q - 1) / tc.block_q;
   a.num_q_tiles = (int32_t)num_q_tiles;
-  const int round_slots = round_slots_for(tc);
+  // the automatic split count needs the device's CU count (one runtime query)
+  const int round_slots = o.kv_splits == 0 ? round_slots_for(tc) : 0;
   const SplitChoice sc = choose_splits(o.kv_splits, num_seqs, num_kv_heads, a.head_blocks,
                                        num_q_tiles, total_q_tokens, tc.block_q, round_slots);
   const int splits = sc.splits;
@@ -1736,7 +1737,8 @@ int prefill_attention_kv_splits(int32_t head_size, int32_t num_heads, int32_t nu
   const int64_t num_q_tiles = ((int64_t)max_q_len + tc.block_q - 1) / tc.block_q;
   return choose_splits(kv_splits, num_seqs, num_kv_heads,
                        num_heads / num_kv_heads / tc.heads_per_tile, num_q_tiles,
-                       total_q_tokens, tc.block_q, round_slots_for(tc)).splits;
+                       total_q_tokens, tc.block_q,
+                       kv_splits == 0 ? round_slots_for(tc) : 0).splits;
 }
 
 uint64_t prefill_attention_workspace_size(int32_t num_heads, int32_t head_size,
