@@ -383,15 +383,25 @@ __device__ WorkItem decode_work(const Args& p, int b, int tid, int nthreads, Seq
       w.split = j >= total - m && j < total;
     }
     for (int sr = 0; sr < S; ++sr) {
-      const int per_tile = Hkv * HBLK;
-      const int per_seq = per_tile * ntiles_by_rank[sr];
+      const int per_tile = Hkv * HBLK;  // (KV head, head block) columns of a Q tile
+      const int nt = ntiles_by_rank[sr];
+      const int per_seq = per_tile * nt;
       if (j < per_seq) {
-        const int z = j / per_tile;
-        const int rem = j - z * per_tile;
+        // Columns go in blocks of 8; within a block, the Q tiles of each column
+        // take consecutive slots of one XCD (item 8 zz + c of the block), so
+        // they stream the column's K/V together and share it in L2.  The tile
+        // order turns by one per block, so that the XCD's four shader engines,
+        // which take its slots in strict rotation, see every tile length.
+        const int cb = j / (8 * nt);
+        const int wdt = min(8, per_tile - cb * 8);
+        const int jj = j - cb * 8 * nt;
+        const int zz = jj / wdt;
+        const int col = cb * 8 + (jj - zz * wdt);
+        const int z = (zz + cb) % nt;
         w.s = order[sr];
-        w.g = rem / HBLK;
-        w.hblk = rem - w.g * HBLK;
-        w.t = ntiles_by_rank[sr] - 1 - z;
+        w.g = col / HBLK;
+        w.hblk = col - w.g * HBLK;
+        w.t = nt - 1 - z;
         w.valid = true;
         return w;
       }
