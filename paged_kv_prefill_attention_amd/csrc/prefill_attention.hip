@@ -301,9 +301,10 @@ struct TileLayout {
 // own L2.  A work item is (sequence s, KV head g, Q tile t, head block); all
 // items of one (s, g) group read the same K/V stream, so they get consecutive
 // slots on one XCD and share its L2.  For up to kSortMaxSeqs sequences the
-// groups are ranked heavy-first (sequences by their key count L, then g) and
-// dealt to the XCDs round-robin by rank; within a group the last (heaviest)
-// Q tile comes first.  Larger batches deal g-major contiguous chunks.
+// sequences are ranked heavy-first by their key count L; within a sequence,
+// blocks of 8 (KV head, head block) columns deal each column's Q tiles to
+// consecutive slots of one XCD, the tile order turned by one per block (see
+// below).  Larger batches deal g-major contiguous chunks.
 // ---------------------------------------------------------------------------
 struct WorkItem {
   int s, g, hblk, t;
@@ -355,11 +356,9 @@ __device__ WorkItem decode_work(const Args& p, int b, int tid, int nthreads, Seq
       ntiles_by_rank[rank] = (key_i - st.ctx[i] + p.block_q - 1) / p.block_q;
     }
     __syncthreads();
-    // Items in heavy-first order (sequences by length; within a sequence the
-    // last Q tile first, the KV heads and head blocks of one Q tile together)
-    // are dealt round-robin over the XCDs: slot k of XCD x is item 8k + x.
-    // Consecutive items of one Q tile are equal work, which suits the strict
-    // rotation in which an XCD hands its workgroups to its shader engines.
+    // Items in heavy-first order of their sequences are dealt round-robin over
+    // the XCDs: slot k of XCD x is item 8k + x.  The order within a sequence
+    // (its Q tiles by column blocks) is set in the enumeration below.
     int j = k * kNumXcd + x;
     if (p.tail_mode) {
       // Tail splitting.  The items past the last whole round (total mod
