@@ -125,6 +125,11 @@ int prefill_attention_validate(const void* q, const void* k_new, const void* v_n
  * prefill_attention_tile_config — the tile geometry prefill_attention uses for this head
  * configuration: *block_q query tokens per Q tile (all heads of a GQA group share a tile) and
  * *block_n keys per KV tile.  The tile bounds below are expressed in these units.  Host-only.
+ * The geometry depends on the head configuration only, never on the page size: query rows and
+ * KV columns of a tile never index the paged cache, each key is resolved to its page on its own
+ * (vLLM PR #54194 report, "Features and motivation", "Implementation breakdown" items 1-2 and
+ * "Key source snippets": the tile selection of context_attention_fwd decoupled from pages).  The
+ * shapes themselves are chosen per head size by measurement on gfx950, not the report's 128/64.
  * Errors: INVALID_ARG (null outputs, bad head counts), UNSUPPORTED (head_size).
  */
 int prefill_attention_tile_config(int32_t head_size, int32_t num_heads, int32_t num_kv_heads,
@@ -272,7 +277,8 @@ int prefill_attention_check_metadata(const int32_t* block_table,
                                      int32_t num_pages, int32_t max_pages_per_seq,
                                      int32_t* flags_out, hipStream_t stream);
 
-/* prefill_attention_strerror — static description of an error code (never NULL). */
+/* prefill_attention_strerror — static description of an error code (never NULL).  No passage
+ * of the pages defines it: it names this library's own error codes. */
 const char* prefill_attention_strerror(int code);
 
 #ifdef __cplusplus

@@ -793,29 +793,27 @@ void prefill_attention_kernel(const KernelArgs p) {
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int i = 0; i < NDB; ++i) oacc[rb][i] = f32x16{};
-  // Scores are accumulated in log2 units (Q is prescaled by scale*log2(e))
-  // and relative to a per-row reference max m_run: the QK^T accumulators start
-  // at -m_run (minit), so p = exp2(acc) needs no further arithmetic.  m_run
-  // only moves when a row's max exceeds it by more than kLazy (factor
-  // 2^kLazy), so the O rescale is rare; numerator and denominator share the
-  // offset, and p <= 2^kLazy stays far from overflow.  A row's m_run is -inf
-  // until its first unmasked key; meanwhile its accumulators start at 0.
+  // Scores s = q.k are accumulated exactly as the MFMA gives them (Q is the
+  // unscaled bf16 input).  The softmax works in log2 units against a per-row
+  // reference max m_run: p = exp2(s * c - m_run) with c = scale * log2(e), one
+  // fp32 FMA per score feeding exp2 (the folding FlashAttention-2 describes,
+  // Dao 2023).  m_run only moves when a row's max exceeds it by more than
+  // kLazy (factor 2^kLazy), so the O rescale is rare; numerator and
+  // denominator share the reference, and p <= 2^kLazy stays far from
+  // overflow.  A row's m_run is -inf until its first unmasked key; meanwhile
+  // its offset mi is 0.
   constexpr float kLazy = 8.f;
+  const float c_log2 = p.scale_log2;
   float m_run[RB], mi[RB], l_run[RB];  // mi = -m_run once the row has one, else 0
   // A tile's row max (relative to m_run) above thr moves m_run: any key at all
   // while the row has none (thr = -inf), else a growth beyond 2^kLazy.
   float thr[RB];
-  // Without registers to spare for the splatted start value (D = 256, or two
-  // row blocks) the offset is added after the product instead.
-  constexpr bool kSplatInit = D <= 128 && RB == 1;
-  f32x16 minit[RB];                    // mi in every element: QK^T accumulator start
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     m_run[rb] = -INFINITY;
     thr[rb] = -INFINITY;
     mi[rb] = 0.f;
     l_run[rb] = 0.f;                   // running row sum (this lane half's keys)
-    minit[rb] = f32x16{};
   }
 
   // Lane-invariant LDS byte offsets of the operand reads (stage 0).
@@ -839,17 +837,14 @@ void prefill_attention_kernel(const KernelArgs p) {
   if (ntile > 0) issue_tile(tb.x, 0);
   if (ntile > 1) issue_tile(tb.x + 1, 1);
 
-  // ---- Q fragments: B operand of S^T = K Q^T, prescaled by scale*log2(e)
+  // ---- Q fragments: B operand of S^T = K Q^T, the exact bf16 input (rows
+  // past the sequence are zero)
   bf16x8 qf[RB][KSTEPS];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const u32x4 v = valid[rb] ? qraw[rb][ks] : u32x4{0, 0, 0, 0};
-      const f32x8 x = __builtin_convertvector(__builtin_bit_cast(bf16x8, v), f32x8);
-      qf[rb][ks] = __builtin_convertvector(x * p.scale_log2, bf16x8);
-    }
-
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      qf[rb][ks] = __builtin_bit_cast(bf16x8, valid[rb] ? qraw[rb][ks] : u32x4{0, 0, 0, 0});
 
   // ---- per-tile pieces
   auto tile_active = [&](int it) __attribute__((always_inline)) {
@@ -886,17 +881,9 @@ void prefill_attention_kernel(const KernelArgs p) {
       for (int rb = 0; rb < RB; ++rb)
         sacc[rb][i % NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8, a), qf[rb][i / NKB],
-            i < NKB ? (kSplatInit ? minit[rb] : f32x16{}) : sacc[rb][i % NKB], 0, 0, 0);
+            i < NKB ? f32x16{} : sacc[rb][i % NKB], 0, 0, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
       if (i + PD < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    if constexpr (!kSplatInit) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[rb][kb][r] += mi[rb];
     }
   };
   // Element mask (boundary tiles only), row max, lazy rescale of O and l.
@@ -934,7 +921,9 @@ void prefill_attention_kernel(const KernelArgs p) {
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) m = fmaxf(m, sacc[rb][kb][r]);
-      mx[rb] = pair_max(m);  // row max relative to the reference
+      // the tile's row max in log2 units, relative to the reference (c > 0, so
+      // the max commutes with the scaling; a fully masked row stays -inf)
+      mx[rb] = fmaf(pair_max(m), c_log2, mi[rb]);
       // (d = 256 has no register to spare for thr and tests m_run instead)
       adj[rb] = D <= 128 ? mx[rb] > thr[rb]
                          : (m_run[rb] == -INFINITY ? mx[rb] > -INFINITY : mx[rb] > kLazy);
@@ -952,22 +941,14 @@ void prefill_attention_kernel(const KernelArgs p) {
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[rb][kb][r] -= d;
         m_run[rb] = unset ? (adj[rb] ? mx[rb] : m_run[rb]) : m_run[rb] + d;
         mi[rb] = m_run[rb] == -INFINITY ? 0.f : -m_run[rb];
         thr[rb] = m_run[rb] == -INFINITY ? -INFINITY : kLazy;
-        if constexpr (kSplatInit) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) minit[rb][r] = mi[rb];
-        }
       }
     }
   };
-  // p = exp2(scale*log2(e)*s - m), row sum, and P^T as bf16 B operands
-  // (PV step ks2 covers keys 16ks2..16ks2+15).
+  // p = exp2(s * scale * log2(e) - m_run) (one FMA into exp2), row sum, and
+  // P^T as bf16 B operands (PV step ks2 covers keys 16ks2..16ks2+15).
   auto expsum = [&](f32x16 (*sacc)[NKB], bf16x8 (*pf)[PSTEPS]) __attribute__((always_inline)) {
     // The row sum adds the bf16-rounded p that the PV product uses.
     const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
@@ -976,7 +957,8 @@ void prefill_attention_kernel(const KernelArgs p) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[rb][kb][r] = __builtin_amdgcn_exp2f(sacc[rb][kb][r]);
+        for (int r = 0; r < 16; ++r)
+          sacc[rb][kb][r] = __builtin_amdgcn_exp2f(fmaf(sacc[rb][kb][r], c_log2, mi[rb]));
 #pragma unroll
       for (int ks2 = 0; ks2 < PSTEPS; ++ks2) {
         const f32x16& sv = sacc[rb][ks2 >> 1];

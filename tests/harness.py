@@ -96,3 +96,19 @@ def sample_rows(n, block_q, rng, extra=8):
         rows = sorted(set(rng.choice(rows, 24, replace=False).tolist()) | {0, n - 1})
     rnd = rng.integers(0, n, size=min(extra, n)).tolist()
     return np.array(sorted(set(rows) | set(rnd)), dtype=np.int64)
+
+
+def edge_rows(w, s, block_q, rng, extra=8):
+    """Rows of sequence ``s`` to compare at full size, with no cap: the first,
+    middle and last row, both edges (and the row after the first edge) of every
+    Q tile, the rows at absolute positions st-1, st, en and en+1 of every
+    multimodal range [st, en] that fall among the new tokens, and ``extra``
+    random rows."""
+    n, c = int(w.q_lens[s]), int(w.ctx_lens[s])
+    cand = {0, n - 1, n // 2}
+    for t in range(0, n, block_q):
+        cand.update({t, t + 1, t + block_q - 1})
+    for st, en in w.mm_list(s):
+        cand.update(a - c for a in (st - 1, st, en, en + 1))
+    cand.update(rng.integers(0, n, size=min(extra, n)).tolist())
+    return np.array(sorted(r for r in cand if 0 <= r < n), dtype=np.int64)

@@ -2,17 +2,18 @@
 
 Bar: |gpu - oracle| <= 2e-2 + 2e-2 * |oracle| elementwise for bf16 outputs;
 tile bounds bit-exact.  The full-size configurations run in the same launch
-configuration as the benchmark and are compared on sampled rows (every head of
-each sampled row) that span tile edges and ragged tails; the small cases are
-compared on every output element.
+configuration as the benchmark: the headline ragged batch is compared on every
+output element, the others on every head of every Q-tile edge row and every
+multimodal-range boundary row; the small cases are compared on every output
+element.
 """
 
 import numpy as np
 import pytest
 
 import oracle
-from tests.harness import (compare, oracle_full, oracle_rows, out_to_f32, run_gpu,
-                           sample_rows, to_device)
+from tests.harness import (compare, edge_rows, oracle_full, oracle_rows, out_to_f32,
+                           run_gpu, to_device)
 from workloads import make_config, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -33,6 +34,8 @@ def tile_q(w):
 
 
 def check_sampled(w, out, seed, cache_only=False, mm_ranges="default", rows_per_seq=None):
+    """Compare every head of each sequence's edge rows (every Q-tile edge, every
+    multimodal-range boundary, random rows) with the oracle."""
     bq, _ = tile_q(w)
     rng = np.random.default_rng(seed)
     worst = (0.0, 0.0)
@@ -40,7 +43,7 @@ def check_sampled(w, out, seed, cache_only=False, mm_ranges="default", rows_per_
         n = int(w.q_lens[s])
         if n == 0:
             continue
-        rows = sample_rows(n, bq, rng)
+        rows = edge_rows(w, s, bq, rng)
         q0 = int(w.query_start_loc[s])
         ref = oracle_rows(w, s, rows, cache_only=cache_only, mm_ranges=mm_ranges)
         e = compare(out[q0 + rows], ref, "%s seq %d" % (w.name, s))
@@ -54,10 +57,21 @@ def test_config1_tiny_full():
     compare(out, oracle_full(w), w.name)
 
 
-@pytest.mark.parametrize("cid,P", [(2, None), (3, 1040), (3, 1056), (4, None), (5, None)],
-                         ids=["c2_page544", "c3_page1040", "c3_page1056", "c4_window",
-                              "c5_mm_prefix"])
-def test_full_size_configs_sampled(cid, P):
+def test_config2_full_outputs():
+    """The headline ragged batch (8 sequences, 544-token pages, 64/64 heads, d=128),
+    in the benchmark's launch configuration: every one of its 3317 x 64 output rows
+    against the oracle."""
+    w = make_config(2)
+    out = out_to_f32(run_gpu(w))
+    err = compare(out, oracle_full(w), w.name)
+    print("%s (all rows) max_abs=%.3g max_rel=%.3g" % (w.name, err[0], err[1]), flush=True)
+
+
+@pytest.mark.parametrize("cid,P", [(3, 1040), (3, 1056), (4, None), (5, None)],
+                         ids=["c3_page1040", "c3_page1056", "c4_window", "c5_mm_prefix"])
+def test_full_size_configs_edge_rows(cid, P):
+    """Full-size configurations: every Q-tile edge row and, on the multimodal
+    workload, the rows at st-1, st, en, en+1 of each of its 60 ranges."""
     w = make_config(cid, page_size=P)
     out = out_to_f32(run_gpu(w))
     assert np.isfinite(out).all()
@@ -109,7 +123,15 @@ FUZZ_PAGES = [1, 7, 16, 128, 512, 544, 1040, 1056, 2048]
 FUZZ_HEADS = [(4, 4), (8, 2), (8, 1), (6, 2), (16, 16), (12, 4), (64, 1), (3, 3)]
 
 
+FUZZ_SIGMAS = [1.0, 1.0, 2.0, 3.0, 4.0]
+FUZZ_SCALES = [1.0, 1.0, 0.5, 2.0]  # times 1/sqrt(d)
+
+
 def fuzz_workload(rng, i, cache_only=False):
+    """Random ragged batch ``i``: 1-4 sequences, page sizes 1..2048 (powers of two and
+    not), head sizes 64/128/256, MHA/GQA/MQA, causal or not, windows, multimodal
+    ranges.  Input magnitude (Q, K ~ N(0, sigma^2), sigma in 1..4) and the scale
+    (0.5, 1 or 2 over sqrt(d)) come from a second stream seeded by ``i``."""
     S = int(rng.integers(1, 5))
     H, Hkv = FUZZ_HEADS[int(rng.integers(0, len(FUZZ_HEADS)))]
     d = int(rng.choice([64, 128, 256]))
@@ -130,23 +152,32 @@ def fuzz_workload(rng, i, cache_only=False):
             for r in range(R):
                 st = int(rng.integers(0, L + 10))
                 mm[s, r] = (st, st + int(rng.choice([0, 3, 40, 150, 400])))
+    mrng = np.random.default_rng(50000 + i)
+    sigma = float(mrng.choice(FUZZ_SIGMAS))
+    scale = float(mrng.choice(FUZZ_SCALES)) / np.sqrt(d)
     return make_workload(seed=9000 + i, ctx_lens=ctx, q_lens=new, num_heads=H,
                          num_kv_heads=Hkv, head_size=d, page_size=P, causal=causal,
                          window_left=wl, window_right=wr, mm_ranges=mm,
-                         new_in_cache=cache_only, name="fuzz%d" % i)
+                         new_in_cache=cache_only, name="fuzz%d" % i, qk_sigma=sigma,
+                         scale=scale)
 
 
-@pytest.mark.parametrize("chunk", range(6))
+@pytest.mark.parametrize("chunk", range(60))
 def test_fuzz_full_outputs(chunk):
-    """60 random ragged batches: page sizes, head sizes, MHA/GQA/MQA, windows, ranges."""
+    """600 random ragged batches (10 per chunk), whole outputs against the oracle:
+    page sizes, head sizes, MHA/GQA/MQA, windows, ranges, input magnitudes and
+    scales; every fourth batch in the cache-sourced mode (k_new = v_new = NULL)."""
     rng = np.random.default_rng(31337 + chunk)
     for i in range(10):
-        w = fuzz_workload(rng, chunk * 10 + i)
-        print("fuzz case", chunk * 10 + i, w.head_size, w.num_heads, w.num_kv_heads,
+        idx = chunk * 10 + i
+        cache_only = idx % 4 == 3
+        w = fuzz_workload(rng, idx, cache_only=cache_only)
+        print("fuzz case", idx, w.head_size, w.num_heads, w.num_kv_heads,
               w.page_size, w.causal, w.window_left, w.window_right,
-              w.max_mm_ranges, flush=True)
-        out = out_to_f32(run_gpu(w))
-        compare(out, oracle_full(w), w.name)
+              w.max_mm_ranges, "cache_only" if cache_only else "split",
+              "scale=%.4g" % w.scale, flush=True)
+        out = out_to_f32(run_gpu(w, cache_only=cache_only))
+        compare(out, oracle_full(w, cache_only=cache_only), w.name)
 
 
 @pytest.mark.parametrize("chunk", range(2))

@@ -41,3 +41,17 @@ def test_config_shapes():
     assert w5.mm_ranges.shape == (1, 60, 2)
     assert ((en - st) == 255).all() and (st[1:] > en[:-1]).all()
     assert st[0] >= 0 and en[-1] <= 16549
+
+
+def test_sigma_one_unchanged_draw():
+    """qk_sigma = 1 gives the plain draw's bits (the benchmark inputs are unchanged);
+    other values widen Q and K only."""
+    kw = dict(seed=5, ctx_lens=[10], q_lens=[7], num_heads=2, num_kv_heads=1,
+              head_size=64, page_size=16, causal=True)
+    a = make_workload(**kw)
+    b = make_workload(qk_sigma=1.0, **kw)
+    c = make_workload(qk_sigma=3.0, **kw)
+    assert np.array_equal(a.q, b.q) and np.array_equal(a.k_cache, b.k_cache)
+    assert np.array_equal(a.v_new, c.v_new)
+    ratio = np.abs(c.f32("q")).mean() / np.abs(a.f32("q")).mean()
+    assert 2.9 < ratio < 3.1

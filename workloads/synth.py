@@ -6,7 +6,8 @@ Recipe (shared by tests, ``smoke()`` and ``bench.py``):
   new-token lengths (inclusive uniform ranges), multimodal-prefix ranges, then
   for every sequence ``q`` [n, H, d], logical ``K`` [L, Hkv, d] and logical
   ``V`` [L, Hkv, d], all N(0, 1) in fp32 and rounded to bf16
-  (round-to-nearest-even).
+  (round-to-nearest-even).  Precision tests widen Q and K to N(0, sigma^2)
+  (``qk_sigma``), which reaches realistic logit magnitudes.
 * The page layout comes from a *separate* stream ``default_rng(table_seed)``:
   a random permutation of the physical pool hands each sequence its pages in
   order.  The pool holds the pages that are needed plus ``spare_frac`` spare
@@ -136,9 +137,12 @@ def make_workload(*, seed: int, table_seed: Optional[int] = None, ctx_lens, q_le
                   block_table_override=None, name: str = "custom",
                   rng: Optional[np.random.Generator] = None, causal_per_seq=None,
                   mm_clamp: bool = True, chunk_size: int = 0,
-                  chunk_lookback: int = -1) -> Workload:
+                  chunk_lookback: int = -1, qk_sigma: float = 1.0) -> Workload:
     """Build a workload from explicit lengths; tensors are drawn from ``rng``
-    (or ``default_rng(seed)``), the page layout from ``default_rng(table_seed)``."""
+    (or ``default_rng(seed)``), the page layout from ``default_rng(table_seed)``.
+
+    ``qk_sigma`` widens Q and K to N(0, qk_sigma^2) before the bf16 rounding
+    (V stays N(0, 1)); with 1.0 the bits are those of the plain draw."""
     ctx_lens = np.asarray(ctx_lens, dtype=np.int32).reshape(-1)
     q_lens = np.asarray(q_lens, dtype=np.int32).reshape(-1)
     assert ctx_lens.shape == q_lens.shape
@@ -159,8 +163,13 @@ def make_workload(*, seed: int, table_seed: Optional[int] = None, ctx_lens, q_le
     logical_k, logical_v = [], []
     for s in range(S):
         n, c, Ls = int(q_lens[s]), int(ctx_lens[s]), int(L[s])
-        qs = f32_to_bf16_bits(rng.standard_normal((n, H, d), dtype=np.float32))
-        ks = f32_to_bf16_bits(rng.standard_normal((Ls, Hkv, d), dtype=np.float32))
+        qf = rng.standard_normal((n, H, d), dtype=np.float32)
+        kf = rng.standard_normal((Ls, Hkv, d), dtype=np.float32)
+        if qk_sigma != 1.0:
+            qf *= np.float32(qk_sigma)
+            kf *= np.float32(qk_sigma)
+        qs = f32_to_bf16_bits(qf)
+        ks = f32_to_bf16_bits(kf)
         vs = f32_to_bf16_bits(rng.standard_normal((Ls, Hkv, d), dtype=np.float32))
         q_bits[qsl[s]:qsl[s + 1]] = qs
         k_new[qsl[s]:qsl[s + 1]] = ks[c:]
