@@ -20,7 +20,8 @@
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
  *    allocates no device memory and keeps no state between calls.  Every call
- *    is re-entrant and thread-safe.
+ *    is re-entrant and thread-safe (prefill_attention_ex_noalloc excepted: it
+ *    uses the library's static scratch, see there).
  *  - bf16 tensors are passed as raw 16-bit patterns, dense, row-major.
  *  - Work is enqueued on `stream` (NULL = the default stream) and the call
  *    returns without synchronising.  A fault during execution surfaces at the
@@ -45,6 +46,7 @@ typedef struct ihipStream_t* hipStream_t;
 #define PAGED_PREFILL_ERR_INVALID_ARG (-1) /* a null required pointer or an out-of-range scalar */
 #define PAGED_PREFILL_ERR_UNSUPPORTED (-2) /* head_size not in {64, 128, 256}, or a size this build does not handle */
 #define PAGED_PREFILL_ERR_HIP (-3)         /* the HIP runtime refused the launch */
+#define PAGED_PREFILL_ERR_SCRATCH (-4)     /* split-KV partials beyond the static scratch (noalloc entry) */
 
 /*
  * prefill_attention — one launch of paged-KV prefill attention over a ragged batch.
@@ -196,6 +198,39 @@ int prefill_attention_ex(const void* q, const void* k_new, const void* v_new,
                          const int32_t* causal_per_seq, int32_t mm_clamp, int32_t chunk_size,
                          int32_t chunk_lookback, int32_t kv_splits, void* workspace,
                          uint64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * prefill_attention_ex_noalloc — prefill_attention_ex for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, arguments and results as prefill_attention_ex without its workspace
+ * arguments.  The split-KV partials live in the library's static scratch, a file-scope device
+ * array of PAGED_PREFILL_NOALLOC_SCRATCH_BYTES bytes that every GPU the library runs on holds
+ * from module load until the process ends; its device address is looked up once per device, on
+ * that device's first call.  The call allocates nothing: no hipMalloc, no hipFree, no allocating
+ * library routine.
+ *   kv_splits  as for prefill_attention_ex.  An explicit count whose partials
+ *              (prefill_attention_workspace_size) exceed the scratch fails with
+ *              PAGED_PREFILL_ERR_SCRATCH before anything is launched; the automatic count (0)
+ *              falls back to no split when its partials would not fit.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last call's contents (no part
+ * of it needs clearing: every partial the merge reads is written by the same call).  Calls that
+ * overlap on one GPU, on different streams or from different threads, race on the scratch; the
+ * caller serialises them (one stream at a time per device).  Errors: as prefill_attention_ex,
+ * plus PAGED_PREFILL_ERR_SCRATCH; HIP_ERROR if the scratch cannot be located on the device.
+ */
+#define PAGED_PREFILL_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int prefill_attention_ex_noalloc(const void* q, const void* k_new, const void* v_new,
+                                 const void* k_cache, const void* v_cache,
+                                 const int32_t* block_table, const int32_t* query_start_loc,
+                                 const int32_t* ctx_lens,
+                                 int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                 int32_t page_size, int32_t window_left, int32_t window_right,
+                                 int32_t causal, const int32_t* mm_ranges, float scale, void* out,
+                                 int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                                 int32_t num_pages, int32_t max_pages_per_seq,
+                                 int32_t max_mm_ranges, const int32_t* causal_per_seq,
+                                 int32_t mm_clamp, int32_t chunk_size, int32_t chunk_lookback,
+                                 int32_t kv_splits, hipStream_t stream);
 
 /*
  * prefill_attention_kv_splits — the split count prefill_attention_ex uses for kv_splits,

@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     BAD_QLEN,
     BAD_QSL,
     ERR_HIP,
+    ERR_SCRATCH,
     ERR_INVALID_ARG,
     ERR_UNSUPPORTED,
     OK,
@@ -20,6 +21,7 @@ from ._binding import (  # noqa: F401
     check_metadata,
     load_library,
     prefill_attention,
+    prefill_attention_ex_noalloc,
     split_count,
     strerror,
     tile_bounds,

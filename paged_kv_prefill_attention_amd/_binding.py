@@ -18,6 +18,7 @@ OK = 0
 ERR_INVALID_ARG = -1
 ERR_UNSUPPORTED = -2
 ERR_HIP = -3
+ERR_SCRATCH = -4
 
 # bits of prefill_attention_check_metadata's result
 BAD_QSL = 1
@@ -45,6 +46,8 @@ _SIGNATURES = {
     "prefill_attention_tile_bounds_ex": ([_P, _P] + [_I] * 6 + [_P] + [_I] * 3
                                          + [_P, _I, _I, _I, _P, _P], _I),
     "prefill_attention_check_metadata": ([_P, _P, _P] + [_I] * 7 + [_P, _P], _I),
+    "prefill_attention_ex_noalloc": ([_P] * 8 + [_I] * 7 + [_P, _F, _P] + [_I] * 6
+                                     + [_P, _I, _I, _I, _I, _P], _I),
 }
 
 _lib = None
@@ -138,23 +141,10 @@ def workspace_size(num_heads: int, head_size: int, total_q_tokens: int, splits: 
                                                                total_q_tokens, splits))
 
 
-def prefill_attention(q, k_new, v_new, k_cache, v_cache, block_table, query_start_loc,
-                      ctx_lens, num_heads: int, num_kv_heads: int, head_size: int,
-                      page_size: int, window_left: int, window_right: int, causal: bool,
-                      mm_ranges, scale: float, out=None, *, max_q_len: Optional[int] = None,
-                      stream=None, causal_per_seq=None, mm_clamp: bool = True,
-                      chunk_size: int = 0, chunk_lookback: int = -1, kv_splits: int = 1,
-                      workspace=None):
-    """Paged-KV prefill attention; returns ``out`` (bf16 [T, H, d]).
-
-    ``k_new = v_new = None`` selects the cache-sourced mode.  ``max_q_len``
-    (the largest new-token count of a sequence) should be passed by callers
-    that know it; when omitted it is read back from ``query_start_loc``,
-    which synchronises the stream.  The keyword-only mask variants and
-    ``kv_splits`` select ``prefill_attention_ex``; with more than one split a
-    workspace is taken from ``workspace`` (a uint8 device tensor) or
-    allocated through torch.
-    """
+def _marshal(q, k_new, v_new, k_cache, v_cache, block_table, query_start_loc, ctx_lens,
+             num_heads, num_kv_heads, head_size, page_size, window_left, window_right, causal,
+             mm_ranges, scale, out, max_q_len, causal_per_seq):
+    """Check the tensors and build the first 24 C arguments; returns (args, out, sizes)."""
     import torch
     H, Hkv, d, P = int(num_heads), int(num_kv_heads), int(head_size), int(page_size)
     T = int(q.shape[0])
@@ -181,6 +171,8 @@ def prefill_attention(q, k_new, v_new, k_cache, v_cache, block_table, query_star
         R = int(mm_ranges.shape[1])
         if R == 0:
             mm_ranges = None
+    if causal_per_seq is not None:
+        _check(causal_per_seq, "causal_per_seq", torch.int32, (S,))
     if out is None:
         out = torch.empty_like(q)
     _check(out, "out", torch.bfloat16, (T, H, d))
@@ -190,6 +182,31 @@ def prefill_attention(q, k_new, v_new, k_cache, v_cache, block_table, query_star
             _ptr(query_start_loc), _ptr(ctx_lens), H, Hkv, d, P, int(window_left),
             int(window_right), int(bool(causal)), _ptr(mm_ranges), float(scale), _ptr(out), S,
             T, int(max_q_len), num_pages, int(block_table.shape[1]), R)
+    return base, out, (S, T, H, Hkv, d, int(max_q_len))
+
+
+def prefill_attention(q, k_new, v_new, k_cache, v_cache, block_table, query_start_loc,
+                      ctx_lens, num_heads: int, num_kv_heads: int, head_size: int,
+                      page_size: int, window_left: int, window_right: int, causal: bool,
+                      mm_ranges, scale: float, out=None, *, max_q_len: Optional[int] = None,
+                      stream=None, causal_per_seq=None, mm_clamp: bool = True,
+                      chunk_size: int = 0, chunk_lookback: int = -1, kv_splits: int = 1,
+                      workspace=None):
+    """Paged-KV prefill attention; returns ``out`` (bf16 [T, H, d]).
+
+    ``k_new = v_new = None`` selects the cache-sourced mode.  ``max_q_len``
+    (the largest new-token count of a sequence) should be passed by callers
+    that know it; when omitted it is read back from ``query_start_loc``,
+    which synchronises the stream.  The keyword-only mask variants and
+    ``kv_splits`` select ``prefill_attention_ex``; with more than one split a
+    workspace is taken from ``workspace`` (a uint8 device tensor) or
+    allocated through torch.
+    """
+    import torch
+    base, out, (S, T, H, Hkv, d, mq) = _marshal(
+        q, k_new, v_new, k_cache, v_cache, block_table, query_start_loc, ctx_lens, num_heads,
+        num_kv_heads, head_size, page_size, window_left, window_right, causal, mm_ranges,
+        scale, out, max_q_len, causal_per_seq)
     plain = (causal_per_seq is None and mm_clamp and chunk_size == 0 and chunk_lookback == -1
              and kv_splits == 1)
     if plain:
@@ -197,9 +214,7 @@ def prefill_attention(q, k_new, v_new, k_cache, v_cache, block_table, query_star
         if rc != OK:
             raise PrefillError(rc, "prefill_attention")
         return out
-    if causal_per_seq is not None:
-        _check(causal_per_seq, "causal_per_seq", torch.int32, (S,))
-    splits = split_count(d, H, Hkv, S, T, int(max_q_len), int(kv_splits))
+    splits = split_count(d, H, Hkv, S, T, mq, int(kv_splits))
     need = workspace_size(H, d, T, splits)
     if need > 0:
         if workspace is None:
@@ -213,6 +228,30 @@ def prefill_attention(q, k_new, v_new, k_cache, v_cache, block_table, query_star
         int(kv_splits), _ptr(workspace), ws_bytes, _stream(stream))
     if rc != OK:
         raise PrefillError(rc, "prefill_attention_ex")
+    return out
+
+
+def prefill_attention_ex_noalloc(q, k_new, v_new, k_cache, v_cache, block_table,
+                                 query_start_loc, ctx_lens, num_heads: int, num_kv_heads: int,
+                                 head_size: int, page_size: int, window_left: int,
+                                 window_right: int, causal: bool, mm_ranges, scale: float,
+                                 out, *, max_q_len: int, stream=None, causal_per_seq=None,
+                                 mm_clamp: bool = True, chunk_size: int = 0,
+                                 chunk_lookback: int = -1, kv_splits: int = 1):
+    """``prefill_attention_ex`` without a workspace: the split-KV partials use the
+    library's static scratch, and nothing is allocated (``out`` and ``max_q_len``
+    are required, so that no tensor is created and the stream is not synchronised)."""
+    if out is None:
+        raise ValueError("prefill_attention_ex_noalloc needs a caller-provided out tensor")
+    base, out, _ = _marshal(
+        q, k_new, v_new, k_cache, v_cache, block_table, query_start_loc, ctx_lens, num_heads,
+        num_kv_heads, head_size, page_size, window_left, window_right, causal, mm_ranges,
+        scale, out, max_q_len, causal_per_seq)
+    rc = load_library().prefill_attention_ex_noalloc(
+        *base, _ptr(causal_per_seq), int(bool(mm_clamp)), int(chunk_size), int(chunk_lookback),
+        int(kv_splits), _stream(stream))
+    if rc != OK:
+        raise PrefillError(rc, "prefill_attention_ex_noalloc")
     return out
 
 

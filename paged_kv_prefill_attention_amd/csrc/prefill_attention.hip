@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "paged_prefill.h"
 
 namespace {
@@ -76,6 +78,12 @@ constexpr int kSortMaxSeqs = 256;  // batches up to this size get heavy-first or
 
 // Rows past the end of a sequence are gathered from here: exact zeros.
 __device__ __attribute__((aligned(16))) uint16_t g_zero_row[256];
+
+// Split-KV partials of the allocation-free entry point (prefill_attention_ex_noalloc).
+// Host code never passes this name to a kernel: it is a host-side stand-in, not a device
+// address.  The device address comes from hipGetSymbolAddress, once per device
+// (scratch_for_current_device below).
+__device__ __attribute__((aligned(256))) unsigned char scratch[PAGED_PREFILL_NOALLOC_SCRATCH_BYTES];
 
 struct KernelArgs {
   const uint16_t* q;
@@ -1339,7 +1347,33 @@ struct Options {
   int32_t kv_splits = 1;
   void* workspace = nullptr;
   uint64_t workspace_bytes = 0;
+  // The workspace is the library's static scratch: an automatic split count
+  // whose partials do not fit falls back to no split, an explicit one fails
+  // with PAGED_PREFILL_ERR_SCRATCH.
+  bool static_scratch = false;
 };
+
+// Device address of `scratch` on the current device, looked up once per device
+// with that device current and kept for every later call.
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+int scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PAGED_PREFILL_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return PAGED_PREFILL_ERR_UNSUPPORTED;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr)
+    return PAGED_PREFILL_ERR_HIP;
+  *ptr = g_scratch_ptr[dev];
+  return PAGED_PREFILL_OK;
+}
 
 constexpr int kMaxSplits = 64;
 
@@ -1537,8 +1571,13 @@ int run(const void* q, const void* k_new, const void* v_new, const void* k_cache
   a.num_q_tiles = (int32_t)num_q_tiles;
   // the automatic split count needs the device's CU count (one runtime query)
   const int round_slots = o.kv_splits == 0 ? round_slots_for(tc) : 0;
-  const SplitChoice sc = choose_splits(o.kv_splits, num_seqs, num_kv_heads, a.head_blocks,
-                                       num_q_tiles, total_q_tokens, tc.block_q, round_slots);
+  SplitChoice sc = choose_splits(o.kv_splits, num_seqs, num_kv_heads, a.head_blocks,
+                                 num_q_tiles, total_q_tokens, tc.block_q, round_slots);
+  if (o.static_scratch && sc.splits > 1 &&
+      workspace_bytes_for(num_heads, head_size, total_q_tokens, sc.splits) > o.workspace_bytes) {
+    if (o.kv_splits != 0) return PAGED_PREFILL_ERR_SCRATCH;
+    sc = {1, 0};  // automatic: the partials would not fit the scratch, so no split
+  }
   const int splits = sc.splits;
   a.kv_splits = splits;
   a.tail_mode = sc.tail;
@@ -1650,6 +1689,8 @@ const char* prefill_attention_strerror(int code) {
     case PAGED_PREFILL_ERR_INVALID_ARG: return "invalid argument";
     case PAGED_PREFILL_ERR_UNSUPPORTED: return "unsupported configuration";
     case PAGED_PREFILL_ERR_HIP: return "HIP runtime error at launch";
+    case PAGED_PREFILL_ERR_SCRATCH:
+      return "split-KV partials exceed the static scratch of prefill_attention_ex_noalloc";
     default: return "unknown error code";
   }
 }
@@ -1714,6 +1755,39 @@ int prefill_attention_ex(const void* q, const void* k_new, const void* v_new,
              make_options(causal_per_seq, mm_clamp, chunk_size, chunk_lookback, kv_splits,
                           workspace, workspace_bytes),
              stream);
+}
+
+int prefill_attention_ex_noalloc(const void* q, const void* k_new, const void* v_new,
+                                 const void* k_cache, const void* v_cache,
+                                 const int32_t* block_table, const int32_t* query_start_loc,
+                                 const int32_t* ctx_lens, int32_t num_heads,
+                                 int32_t num_kv_heads, int32_t head_size, int32_t page_size,
+                                 int32_t window_left, int32_t window_right, int32_t causal,
+                                 const int32_t* mm_ranges, float scale, void* out,
+                                 int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                                 int32_t num_pages, int32_t max_pages_per_seq,
+                                 int32_t max_mm_ranges, const int32_t* causal_per_seq,
+                                 int32_t mm_clamp, int32_t chunk_size, int32_t chunk_lookback,
+                                 int32_t kv_splits, hipStream_t stream) {
+  // the host-side argument checks first, so that a bad call needs no device
+  int rc = validate(q, k_new, v_new, k_cache, v_cache, block_table, query_start_loc, ctx_lens,
+                    num_heads, num_kv_heads, head_size, page_size, window_left, window_right,
+                    causal, mm_ranges, scale, out, num_seqs, total_q_tokens, max_q_len,
+                    num_pages, max_pages_per_seq, max_mm_ranges);
+  if (rc != PAGED_PREFILL_OK) return rc;
+  Options o = make_options(causal_per_seq, mm_clamp, chunk_size, chunk_lookback, kv_splits,
+                           nullptr, PAGED_PREFILL_NOALLOC_SCRATCH_BYTES);
+  o.static_scratch = true;
+  rc = validate_mask_options(o);
+  if (rc != PAGED_PREFILL_OK) return rc;
+  if (kv_splits < 0 || kv_splits > kMaxSplits) return PAGED_PREFILL_ERR_INVALID_ARG;
+  if (num_seqs == 0 || total_q_tokens == 0 || max_q_len == 0) return PAGED_PREFILL_OK;
+  rc = scratch_for_current_device(&o.workspace);
+  if (rc != PAGED_PREFILL_OK) return rc;
+  return run(q, k_new, v_new, k_cache, v_cache, block_table, query_start_loc, ctx_lens,
+             num_heads, num_kv_heads, head_size, page_size, window_left, window_right, causal,
+             mm_ranges, scale, out, num_seqs, total_q_tokens, max_q_len, num_pages,
+             max_pages_per_seq, max_mm_ranges, o, stream);
 }
 
 int prefill_attention_kv_splits(int32_t head_size, int32_t num_heads, int32_t num_kv_heads,

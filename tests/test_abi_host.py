@@ -113,6 +113,26 @@ def test_strerror(lib):
     assert "invalid" in ppa.strerror(-1)
     assert "unsupported" in ppa.strerror(-2)
     assert "unknown" in ppa.strerror(7)
+    assert "scratch" in ppa.strerror(ppa.ERR_SCRATCH)
+
+
+def test_noalloc_rejects_bad_arguments_before_touching_a_device(lib):
+    """The allocation-free entry point runs the host checks (arguments, mask options,
+    split count) before it looks its scratch up on the device, so these calls need
+    no GPU; an empty batch returns OK without a launch."""
+    import ctypes
+    P = [None] * 8
+    common = (8, 2, 128, 16, -1, -1, 1, None, 0.1, None, 0, 0, 0, 1, 1, 0)
+    assert lib.prefill_attention_ex_noalloc(*P, *common, None, 1, 0, -1, 1, None) == 0
+    F = [ctypes.c_void_p(4096 * (i + 1)) for i in range(8)]
+    nonempty = (8, 2, 128, 16, -1, -1, 1, None, 0.1, ctypes.c_void_p(1 << 20), 1, 10, 10, 1,
+                1, 0)
+    for bad in [(None, 2, 0, -1, 1), (None, 1, -1, -1, 1), (None, 1, 16, -2, 1),
+                (None, 1, 0, -1, -1), (None, 1, 0, -1, 65)]:
+        assert lib.prefill_attention_ex_noalloc(*F, *nonempty, *bad, None) == ppa.ERR_INVALID_ARG
+    bad_heads = (6, 4) + nonempty[2:]
+    assert lib.prefill_attention_ex_noalloc(*F, *bad_heads, None, 1, 0, -1, 1, None) == \
+        ppa.ERR_INVALID_ARG
 
 
 def test_invalid_ex_options_return_before_launch(lib):
