@@ -1027,15 +1027,31 @@ void prefill_attention_kernel(const KernelArgs p) {
   for (int i = 0; 2 * i < ntile; ++i) {
     vm_wait<0>();
     block_barrier();
-    if (2 * i + 2 < ntile) issue_tile(tb.x + 2 * i + 2, (2 * i + 2) % NSTAGE);
-    if (2 * i + 3 < ntile) issue_tile(tb.x + 2 * i + 3, (2 * i + 3) % NSTAGE);
+    // d <= 128: the copy of tile 2i + 2 + h goes behind the QK^T MFMAs of
+    // tile 2i + h, so the workgroup's copies do not all queue for the address
+    // unit right after the barrier.  (d = 256 issues both here: the live
+    // scores would spill.)
+    constexpr bool kCopyAfterQk = D <= 128;
+    if constexpr (!kCopyAfterQk) {
+      if (2 * i + 2 < ntile) issue_tile(tb.x + 2 * i + 2, (2 * i + 2) % NSTAGE);
+      if (2 * i + 3 < ntile) issue_tile(tb.x + 2 * i + 3, (2 * i + 3) % NSTAGE);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int it = 2 * i + h;
-      if ((pair && h != khalf) || it >= ntile || !tile_active(it)) continue;
+      const bool run = !((pair && h != khalf) || it >= ntile || !tile_active(it));
+      if constexpr (!kCopyAfterQk) {
+        if (!run) continue;
+      }
       f32x16 sacc[RB][NKB];
       bf16x8 pf[RB][PSTEPS];
-      qk(it % NSTAGE, sacc);
+      if constexpr (kCopyAfterQk) {
+        if (run) qk(it % NSTAGE, sacc);
+        if (2 * i + 2 + h < ntile) issue_tile(tb.x + 2 * i + 2 + h, (2 * i + 2 + h) % NSTAGE);
+        if (!run) continue;
+      } else {
+        qk(it % NSTAGE, sacc);
+      }
       mask_rowmax(it, sacc);
       expsum(sacc, pf);
       pv(it % NSTAGE, pf);
