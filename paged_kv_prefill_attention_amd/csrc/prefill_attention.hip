@@ -67,7 +67,7 @@ constexpr int kSortMaxSeqs = 256;  // batches up to this size get heavy-first or
 // of the LDS ring, wavefronts per SIMD, and 32-row query blocks per wavefront.
 // Overridable at build time (-DPREFILL_TILE_D128=4,64,4,1,2) for sweeps.
 #ifndef PREFILL_TILE_D64
-#define PREFILL_TILE_D64 4, 64, 4, 2, 1
+#define PREFILL_TILE_D64 4, 32, 4, 4, 1
 #endif
 #ifndef PREFILL_TILE_D128
 #define PREFILL_TILE_D128 8, 64, 4, 2, 1
@@ -449,9 +449,10 @@ struct TileShape {
   static constexpr int DMA_PER_TENSOR = BN * D * 2 / 1024;  // 1-KB copies per tile per tensor
   static constexpr int DMA_PER_WAVE = DMA_PER_TENSOR / NW;
   static constexpr int LDS_BYTES = NSTAGE * 2 * BN * D * 2;
-  // Block-table entries staged in LDS per workgroup (one workgroup per CU
-  // when the ring is large, two otherwise).
-  static constexpr int BT_CACHE = LDS_BYTES >= 96 * 1024 ? 4096 : 2048;
+  // Block-table entries staged in LDS per workgroup: sized so that the
+  // workgroups a CU holds (one with a large ring, two with a medium one, four
+  // with a 32 KiB ring at four wavefronts per SIMD) fit its 160 KiB.
+  static constexpr int BT_CACHE = WPE_ >= 4 ? 512 : (LDS_BYTES >= 96 * 1024 ? 4096 : 2048);
   // KV-pair mode (short Q tiles): the two halves of the workgroup exchange
   // their partial results through the ring, NW/2 x 64 lanes x (O, m, l).
   static constexpr int XREGS = RB * (D / 32 * 16 + 2);

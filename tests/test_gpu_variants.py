@@ -214,7 +214,7 @@ def test_short_last_tiles_split_kv_tiles_between_halves(d, heads, splits):
 
 @pytest.mark.parametrize("d,n,causal,wl,wr,note", [
     (128, 256 * 66, True, 511, -1, "528 items: last 16 split"),
-    (64, 128 * 130, False, 64, 64, "1040 items, two workgroups per CU: last 16 split"),
+    (64, 128 * 258, False, 64, 64, "2064 items, four workgroups per CU: last 16 split"),
 ])
 def test_tail_splitting_automatic(d, n, causal, wl, wr, note):
     """Automatic split count on batches of two to four rounds of items: the kernel cuts
