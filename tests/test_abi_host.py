@@ -95,9 +95,9 @@ def test_invalid_call_returns_before_launch(lib):
 
 
 def test_tile_config(lib):
-    # 8 wavefronts x 32 rows for head sizes 128/256, 4 x 32 rows for 64
+    # 8 wavefronts x 32 rows for head sizes 128/256, 4 x 32 rows for 64 (32-key tiles)
     assert ppa.tile_config(128, 64, 64) == (256, 64)
-    assert ppa.tile_config(64, 8, 8) == (128, 64)
+    assert ppa.tile_config(64, 8, 8) == (128, 32)
     assert ppa.tile_config(256, 8, 2) == (64, 32)     # 4 query heads share a tile
     assert ppa.tile_config(256, 16, 8) == (128, 32)
     assert ppa.tile_config(128, 64, 1) == (4, 64)     # MQA: 64 heads x 4 tokens
@@ -165,8 +165,9 @@ def test_split_count_and_workspace_size(lib):
     assert ppa.split_count(256, 8, 2, 8, 10155, 2048, 0) == 2
     # two to four rounds of items with a last round at most a quarter full: tail splitting
     assert ppa.split_count(256, 16, 8, 1, 12454, 12454, 0) == 4   # 784 items, 16 past 3 rounds
-    assert ppa.split_count(64, 8, 8, 1, 16640, 16640, 0) == 4     # 1040 items, 512 per round
-    assert ppa.split_count(64, 8, 8, 1, 16384, 16384, 0) == 1     # 1024 items: whole rounds
+    assert ppa.split_count(64, 8, 8, 1, 33024, 33024, 0) == 4     # 2064 items, 1024 per round
+    assert ppa.split_count(64, 8, 8, 1, 32768, 32768, 0) == 1     # 2048 items: whole rounds
+    assert ppa.split_count(64, 8, 8, 1, 16384, 16384, 0) == 2     # 1024 items: one round
     assert ppa.split_count(256, 8, 2, 8, 1 << 20, 2048, 0) == 1   # 512 items: whole rounds
     assert ppa.split_count(128, 8, 8, 1, 256 * 80, 256 * 80, 0) == 1  # tail of 128: too full
     assert ppa.split_count(128, 64, 64, 8, 1 << 20, 1024, 0) == 1  # 2048 items: no split
