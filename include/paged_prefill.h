@@ -236,9 +236,10 @@ int prefill_attention_ex_noalloc(const void* q, const void* k_new, const void* v
  * prefill_attention_kv_splits — the split count prefill_attention_ex uses for kv_splits,
  * and so the workspace it needs.  kv_splits > 0: kv_splits itself.  kv_splits = 0
  * (automatic), with W the workgroups the GPU runs at once (CUs times the workgroups of this
- * head size that one CU holds: 256 or 512 on MI355X) and the Q-tile work items bounded from
+ * head size that one CU holds: 256 or 1024 on MI355X) and the Q-tile work items bounded from
  * the sizes alone (at most num_seqs * cdiv(max_q_len, block_q) Q tiles, and at most
  * (total_q_tokens + num_seqs * (block_q - 1)) / block_q, times the KV heads):
+ *   - a whole number of rounds (a multiple of W, at least W items): 1;
  *   - fewer than 2W items: enough segments for about 2W workgroups, at most 16; every item
  *     longer than its share is cut;
  *   - 2W to 4W items whose last round is at most a quarter full (num_seqs <= 256): 4, and

@@ -3,8 +3,10 @@
 // One workgroup owns one Q tile: `block_q` query tokens of one sequence times
 // the `heads_per_tile` query heads of one GQA group, packed into 32 MFMA rows
 // per wavefront (256 rows for 8 wavefronts), so one K/V gather serves every
-// head of the group.  Work items are ranked heavy-first and dealt
-// round-robin over the XCDs.  The workgroup walks the KV tiles
+// head of the group.  Sequences are ranked heavy-first; a sequence's work
+// items go in blocks of 8 (KV head, head block) columns, the Q tiles of one
+// column on consecutive slots of one XCD (slot k of XCD x is item 8k + x).
+// The workgroup walks the KV tiles
 // [lo, hi) given by the tile bound calculator (the window unioned with every
 // multimodal range that overlaps the tile's queries; vLLM PR #50776 report,
 // "Key source snippets"; vLLM PR #53147 report, "Implementation breakdown"
@@ -370,10 +372,12 @@ __device__ WorkItem decode_work(const Args& p, int b, int tid, int nthreads, Seq
     int j = k * kNumXcd + x;
     if (p.tail_mode) {
       // Tail splitting.  The items past the last whole round (total mod
-      // round_slots of them, the lightest) would run alone at the end; when
-      // they fill at most a quarter of a round, the last m of them are cut
-      // into kv_splits segments: segment 0 in the item's own slot, the others
-      // in the helper slots that follow the main ones.
+      // round_slots of them: the last in the order below, so those of the
+      // lightest sequences, though within a column block the tile order is
+      // rotated and they need not be the lightest tiles) would run alone at
+      // the end; when they fill at most a quarter of a round, the last m of
+      // them are cut into kv_splits segments: segment 0 in the item's own
+      // slot, the others in the helper slots that follow the main ones.
       int total = 0;
       for (int sr = 0; sr < S; ++sr) total += ntiles_by_rank[sr];
       total *= Hkv * HBLK;
@@ -398,7 +402,10 @@ __device__ WorkItem decode_work(const Args& p, int b, int tid, int nthreads, Seq
         // take consecutive slots of one XCD (item 8 zz + c of the block), so
         // they stream the column's K/V together and share it in L2.  The tile
         // order turns by one per block, so that the XCD's four shader engines,
-        // which take its slots in strict rotation, see every tile length.
+        // which take its slots in strict rotation, see every tile length.  A
+        // last block of wdt < 8 columns (columns per Q tile not a multiple of
+        // 8) lays its items out as wdt zz + c: there a column's Q tiles are
+        // spread over XCDs and do not share L2.
         const int cb = j / (8 * nt);
         const int wdt = min(8, per_tile - cb * 8);
         const int jj = j - cb * 8 * nt;
@@ -1463,6 +1470,8 @@ int64_t item_slots(int num_seqs, int num_kv_heads, int64_t num_q_tiles, int head
 // at most num_seqs * cdiv(max_q_len, block_q) and at most sum over s of
 // cdiv(n_s, block_q) <= (T + S (block_q - 1)) / block_q; times the KV heads and
 // head blocks, that bounds the work items.  Automatic choice:
+//  - a whole number of rounds (at least one): no split, there is no partial
+//    round to even out;
 //  - fewer than twice round_slots items: split every long item (the segment-cap
 //    rule), to about 2 * round_slots workgroups, at most 16 segments;
 //  - two to four rounds of items whose bound leaves a last round at most a
@@ -1484,6 +1493,7 @@ SplitChoice choose_splits(int kv_splits, int num_seqs, int num_kv_heads, int hea
       ((int64_t)total_q_tokens + (int64_t)num_seqs * (block_q - 1)) / block_q);
   const int64_t items = tiles * num_kv_heads * head_blocks;
   if (items <= 0) return {1, 0};
+  if (items >= round_slots && items % round_slots == 0) return {1, 0};
   if (items < 2 * (int64_t)round_slots)
     return {(int)std::min<int64_t>(16, (2 * (int64_t)round_slots + items - 1) / items), 0};
   const int64_t tail = items % round_slots;

@@ -167,7 +167,8 @@ def test_split_count_and_workspace_size(lib):
     assert ppa.split_count(256, 16, 8, 1, 12454, 12454, 0) == 4   # 784 items, 16 past 3 rounds
     assert ppa.split_count(64, 8, 8, 1, 33024, 33024, 0) == 4     # 2064 items, 1024 per round
     assert ppa.split_count(64, 8, 8, 1, 32768, 32768, 0) == 1     # 2048 items: whole rounds
-    assert ppa.split_count(64, 8, 8, 1, 16384, 16384, 0) == 2     # 1024 items: one round
+    assert ppa.split_count(64, 8, 8, 1, 16384, 16384, 0) == 1     # 1024 items: one round
+    assert ppa.split_count(64, 8, 8, 1, 16640, 16640, 0) == 2     # 1040 items: 1 round + 16
     assert ppa.split_count(256, 8, 2, 8, 1 << 20, 2048, 0) == 1   # 512 items: whole rounds
     assert ppa.split_count(128, 8, 8, 1, 256 * 80, 256 * 80, 0) == 1  # tail of 128: too full
     assert ppa.split_count(128, 64, 64, 8, 1 << 20, 1024, 0) == 1  # 2048 items: no split
