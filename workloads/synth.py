@@ -321,13 +321,19 @@ def make_named(name: str) -> Workload:
 # Workloads a tile-shape sweep times: the benchmark shapes of each head size,
 # the ragged batch at head size 64, and a dense non-causal batch (no masking,
 # no ragged tails) that isolates the tile loop.
+# The page-size rows (1056 and the power of two 512 or 1024 beside 544 and 1040)
+# show whether the best shape depends on the page size as well as the head size.
 TILE_SWEEP = ["ragged_batch_page544", "gqa_d256_page1040", "sliding_window_16k",
-              "window_clamped_mm_prefix", "ragged_batch_page544_d64", "dense_noncausal_d128"]
+              "window_clamped_mm_prefix", "ragged_batch_page544_d64", "dense_noncausal_d128",
+              "ragged_batch_page1056", "ragged_batch_page512", "gqa_d256_page1056",
+              "gqa_d256_page1024"]
 
 
 def make_sweep(name: str) -> Workload:
     configs = {"ragged_batch_page544": (2, None), "gqa_d256_page1040": (3, 1040),
-               "sliding_window_16k": (4, None), "window_clamped_mm_prefix": (5, None)}
+               "sliding_window_16k": (4, None), "window_clamped_mm_prefix": (5, None),
+               "ragged_batch_page1056": (2, 1056), "ragged_batch_page512": (2, 512),
+               "gqa_d256_page1056": (3, 1056), "gqa_d256_page1024": (3, 1024)}
     if name in configs:
         cid, P = configs[name]
         return make_config(cid, page_size=P)
