@@ -1053,16 +1053,27 @@ void prefill_attention_kernel(const KernelArgs p) {
       }
       f32x16 sacc[RB][NKB];
       bf16x8 pf[RB][PSTEPS];
+      // Wave priority: 2 while the tile's QK^T MFMAs issue, 1 for the rest of
+      // the tile, 0 after it.  The arbiter then favours a wavefront that is
+      // starting a tile over its SIMD partner, whose softmax fills the matrix
+      // pipe's shadow, and a wavefront in its tile over one between tiles.
       if constexpr (kCopyAfterQk) {
-        if (run) qk(it % NSTAGE, sacc);
+        if (run) {
+          __builtin_amdgcn_s_setprio(2);
+          qk(it % NSTAGE, sacc);
+          __builtin_amdgcn_s_setprio(1);
+        }
         if (2 * i + 2 + h < ntile) issue_tile(tb.x + 2 * i + 2 + h, (2 * i + 2 + h) % NSTAGE);
         if (!run) continue;
       } else {
+        __builtin_amdgcn_s_setprio(2);
         qk(it % NSTAGE, sacc);
+        __builtin_amdgcn_s_setprio(1);
       }
       mask_rowmax(it, sacc);
       expsum(sacc, pf);
       pv(it % NSTAGE, pf);
+      __builtin_amdgcn_s_setprio(0);
     }
   }
   if (pair) {
