@@ -14,6 +14,12 @@ mean; the median, extremes and the first-to-last event span per step are
 reported beside it.  ``cpu_baseline`` times the CPU oracle on a bounded sample
 of the same workload.
 
+Before the warm-up steps the GPU runs the same launch back to back for
+``--prewarm-ms`` (default 200 ms, untimed, reported as ``prewarm_ms``): coming
+out of idle its clock ramps up over the first tens of milliseconds of load,
+and launches in that window run up to 40% slower than at steady state, which
+a handful of warm-up steps does not cover.
+
 ``--suite FILE`` additionally times every configuration and the sliding-window
 length sweep and writes them to FILE (one JSON object per line).
 
@@ -73,6 +79,17 @@ def traffic_from_profiles(workload: str):
     if not m_hash or not m_val or m_hash.group(1) != kernel_source_hash():
         return None
     return float(m_val.group(1))
+
+
+def prewarm(fn, ms: float):
+    """Launch ``fn`` back to back, untimed, for about ``ms`` milliseconds of
+    wall time, so that the timed steps run at the GPU's loaded clock."""
+    import torch
+    t_end = time.perf_counter() + ms / 1e3
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
 
 
 def time_launches(fn, steps: int, warmup: int):
@@ -250,7 +267,7 @@ def cpu_baseline(w, heads: int, min_seconds: float = 10.0, max_passes: int = 8):
                           len(os.sched_getaffinity(0)), threads)}
 
 
-def run_suite(path, steps, warmup):
+def run_suite(path, steps, warmup, prewarm_ms=0.0):
     """Every configuration plus the sliding-window length sweep."""
     import torch
     from workloads import NAMED, make_config, make_named
@@ -267,6 +284,8 @@ def run_suite(path, steps, warmup):
         w = make_named(cid) if isinstance(cid, str) else make_config(cid, page_size=P,
                                                                       new_tokens=n)
         fn, dev, out = make_launcher(w, kv_splits=splits)
+        if not rows:
+            prewarm(fn, prewarm_ms)
         ms, per, _ = time_launches(fn, steps, warmup)
         per.sort()
         ms_dev = time_graph(fn, max(3, steps // 5), 2)
@@ -290,7 +309,7 @@ def run_suite(path, steps, warmup):
             f.write(json.dumps(r) + "\n")
 
 
-def run_tile_sweep(path, steps, warmup):
+def run_tile_sweep(path, steps, warmup, prewarm_ms=0.0):
     """Eager timing of the tile-sweep workloads, in the order of TILE_SWEEP
     (under a counter profiler each workload is warmup + steps dispatches)."""
     import torch
@@ -300,6 +319,8 @@ def run_tile_sweep(path, steps, warmup):
     for name in TILE_SWEEP:
         w = make_sweep(name)
         fn, dev, out = make_launcher(w)
+        if not rows:
+            prewarm(fn, prewarm_ms)
         ms, per, _ = time_launches(fn, steps, warmup)
         per.sort()
         bq, bn = ppa.tile_config(w.head_size, w.num_heads, w.num_kv_heads)
@@ -321,6 +342,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prewarm-ms", type=float, default=200.0,
+                    help="untimed back-to-back launches before the warm-up steps (ms)")
     ap.add_argument("--cpu-heads", type=int, default=64,
                     help="query heads in the bounded CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -351,7 +374,7 @@ def main():
     torch.cuda.set_device(0)
 
     if args.tile_sweep:
-        run_tile_sweep(args.tile_sweep, args.steps, args.warmup)
+        run_tile_sweep(args.tile_sweep, args.steps, args.warmup, args.prewarm_ms)
         return
 
     if args.copy_bytes:
@@ -366,6 +389,7 @@ def main():
     fn, dev, out = make_launcher(w)
     flop = useful_flop(w)
     torch.cuda.synchronize()
+    prewarm(fn, args.prewarm_ms)
     span_ms, per, wall = time_launches(fn, args.steps, args.warmup)
     # One timing for every figure: a step is one launch, timed by HIP events on
     # the launch stream; value, pct_bf16_peak and the roofline all use their mean.
@@ -377,7 +401,8 @@ def main():
     bq, bn = ppa.tile_config(w.head_size, w.num_heads, w.num_kv_heads)
     rec = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "steps": args.steps, "warmup": args.warmup, "prewarm_ms": args.prewarm_ms,
+        "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_heads": w.num_heads,
@@ -402,7 +427,7 @@ def main():
     del dev, out, fn
     torch.cuda.empty_cache()
     if args.suite:
-        run_suite(args.suite, args.steps, args.warmup)
+        run_suite(args.suite, args.steps, args.warmup, args.prewarm_ms)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, min(args.cpu_heads, w.num_heads))
     else:
