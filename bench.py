@@ -16,9 +16,10 @@ of the same workload.
 
 Before the warm-up steps the GPU runs the same launch back to back for
 ``--prewarm-ms`` (default 200 ms, untimed, reported as ``prewarm_ms``): coming
-out of idle its clock ramps up over the first tens of milliseconds of load,
-and launches in that window run up to 40% slower than at steady state, which
-a handful of warm-up steps does not cover.
+out of idle, or after light work, its clock ramps up over the first tens of
+milliseconds of load, and launches in that window run up to 40% slower than at
+steady state, which a handful of warm-up steps does not cover.  The suite and
+the tile sweep do the same before every workload.
 
 ``--suite FILE`` additionally times every configuration and the sliding-window
 length sweep and writes them to FILE (one JSON object per line).
@@ -284,8 +285,7 @@ def run_suite(path, steps, warmup, prewarm_ms=0.0):
         w = make_named(cid) if isinstance(cid, str) else make_config(cid, page_size=P,
                                                                       new_tokens=n)
         fn, dev, out = make_launcher(w, kv_splits=splits)
-        if not rows:
-            prewarm(fn, prewarm_ms)
+        prewarm(fn, prewarm_ms)
         ms, per, _ = time_launches(fn, steps, warmup)
         per.sort()
         ms_dev = time_graph(fn, max(3, steps // 5), 2)
@@ -319,8 +319,7 @@ def run_tile_sweep(path, steps, warmup, prewarm_ms=0.0):
     for name in TILE_SWEEP:
         w = make_sweep(name)
         fn, dev, out = make_launcher(w)
-        if not rows:
-            prewarm(fn, prewarm_ms)
+        prewarm(fn, prewarm_ms)
         ms, per, _ = time_launches(fn, steps, warmup)
         per.sort()
         bq, bn = ppa.tile_config(w.head_size, w.num_heads, w.num_kv_heads)
