@@ -270,10 +270,12 @@ def test_large_batch_without_sequence_sort(d):
     compare(out_to_f32(run_gpu(w)), oracle_full(w), w.name)
 
 
-@pytest.mark.parametrize("d,ctx,page", [(64, 5000, 1), (128, 9000, 1), (64, 7000, 3)])
+@pytest.mark.parametrize("d,ctx,page", [(64, 5000, 1), (128, 9000, 1), (64, 7000, 3),
+                                        (64, 480, 1), (64, 560, 1)])
 def test_block_table_beyond_lds_cache(d, ctx, page):
     """A work item whose KV range covers more pages than the LDS block-table cache
-    holds (2048 entries at d=64, 4096 at d=128): pages are read on the scalar unit,
+    holds (512 entries at d=64, 4096 at d=128; the d=64 cases at 480 and 560 cached
+    tokens sit on either side of the limit): pages are read on the scalar unit,
     with copies that straddle page boundaries and the cache/new-token edge.  Whole
     outputs, plain and split-KV."""
     w = make_workload(seed=4500 + d + page, ctx_lens=[ctx, 40], q_lens=[200, 30],
