@@ -194,14 +194,15 @@ def test_split_kv_rejects_missing_workspace():
 def test_short_last_tiles_split_kv_tiles_between_halves(d, heads, splits):
     """Short last Q tiles (at most half the tile's rows valid, two or more KV tiles):
     the two halves of the workgroup take alternate KV tiles and are merged at the end.
-    Lengths straddle the half-tile boundary and include one-token chunks; causal, windowed
-    and bidirectional masks; whole outputs against the oracle."""
+    Lengths straddle the half- and quarter-tile boundaries and include one-token chunks;
+    causal, windowed and bidirectional masks; whole outputs against the oracle."""
     import paged_kv_prefill_attention_amd as ppa
     H, Hkv = heads
     bq, _ = ppa.tile_config(d, H, Hkv)
     half = bq // 2
-    q_lens = [1, half - 1, half, half + 1, bq + half, 2 * bq + 7]
-    ctx = [700, 64, 1, 333, 900, 0]
+    qtr = bq // 4
+    q_lens = [1, half - 1, half, half + 1, bq + half, 2 * bq + 7, qtr - 1, qtr, qtr + 1]
+    ctx = [700, 64, 1, 333, 900, 0, 520, 3, 1200]
     for i, (causal, wl, wr) in enumerate([(True, -1, -1), (True, 100, -1), (False, 80, 40)]):
         w = make_workload(seed=9100 + 10 * i + splits, ctx_lens=ctx, q_lens=q_lens,
                           num_heads=H, num_kv_heads=Hkv, head_size=d, page_size=16,
