@@ -12,7 +12,8 @@ allowed (query, key) pair per query head, divided by the mean time per step
 inputs resident in HBM).  ``pct_bf16_peak`` and ``roofline`` use that same
 mean; the median, extremes and the first-to-last event span per step are
 reported beside it.  ``cpu_baseline`` times the CPU oracle on a bounded sample
-of the same workload.
+of the same workload, ``cpu_baseline_pruned`` the same oracle restricted to each
+Q tile's KV-tile bounds.
 
 Before the warm-up steps the GPU runs the same launch back to back for
 ``--prewarm-ms`` (default 200 ms, untimed, reported as ``prewarm_ms``): coming
@@ -268,6 +269,45 @@ def cpu_baseline(w, heads: int, min_seconds: float = 10.0, max_passes: int = 8):
                           len(os.sched_getaffinity(0)), threads)}
 
 
+def cpu_baseline_pruned(w, heads: int, block_q: int, block_n: int, min_seconds: float = 5.0,
+                        max_passes: int = 8):
+    """The same oracle restricted, per Q tile of the kernel's geometry, to the keys
+    of that tile's bounds (``key_range`` from ``oracle.tile_bounds_ref``): the
+    CPU counterpart of the kernel's tile pruning, timed like ``cpu_baseline``."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = 1
+    args = (w.f32("q"), w.f32("k_new"), w.f32("v_new"), w.f32("k_cache"), w.f32("v_cache"),
+            w.block_table, w.query_start_loc, w.ctx_lens, w.num_heads, w.num_kv_heads,
+            w.head_size, w.page_size, w.window_left, w.window_right, w.causal, w.mm_ranges,
+            w.scale)
+    t0 = time.perf_counter()
+    passes = 0
+    while passes < max_passes:
+        for s in range(w.num_seqs):
+            n, c = int(w.q_lens[s]), int(w.ctx_lens[s])
+            for t in range(-(-n // block_q)):
+                lo, hi = oracle.tile_bounds_ref(c, n, t, block_q, block_n, w.causal,
+                                                w.window_left, w.window_right, w.mm_list(s))
+                rows = np.arange(t * block_q, min(n, (t + 1) * block_q))
+                oracle.reference_rows(*args, s, rows, heads=range(heads),
+                                      key_range=(lo * block_n, min(hi * block_n, c + n)))
+        passes += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    el = time.perf_counter() - t0
+    flop = useful_flop(w) * heads // w.num_heads * passes
+    return {"value": flop / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle, keys pruned to the tile bounds",
+            "sample": "fp32 numpy oracle per Q tile of %d tokens over its %d-key tile range, "
+                      "query heads 0..%d of all %d sequences, %d pass(es), %.1f s" % (
+                          block_q, block_n, heads - 1, w.num_seqs, passes, el)}
+
+
 def run_suite(path, steps, warmup, prewarm_ms=0.0):
     """Every configuration plus the sliding-window length sweep."""
     import torch
@@ -281,6 +321,8 @@ def run_suite(path, steps, warmup, prewarm_ms=0.0):
     cases += [(3, 1040, None, 2), (3, 1040, None, 4), (3, 1040, None, 0), (5, None, None, 0)]
     cases += [(name, None, None, k) for name in NAMED for k in
               ((1, 0) if name == "long_context_short_chunk" else (1,))]
+    # the window's pruning, for contrast: config 4 attending to every key
+    cases += [("sliding_window_16k_full", None, None, 1)]
     for cid, P, n, splits in cases:
         w = make_named(cid) if isinstance(cid, str) else make_config(cid, page_size=P,
                                                                       new_tokens=n)
@@ -429,6 +471,8 @@ def main():
         run_suite(args.suite, args.steps, args.warmup, args.prewarm_ms)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, min(args.cpu_heads, w.num_heads))
+        rec["cpu_baseline_pruned"] = cpu_baseline_pruned(w, min(args.cpu_heads, w.num_heads),
+                                                         bq, bn)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

@@ -311,6 +311,14 @@ def make_named(name: str) -> Workload:
         return make_workload(seed=2003, ctx_lens=c2.ctx_lens, q_lens=c2.q_lens, num_heads=64,
                              num_kv_heads=64, head_size=64, page_size=544, causal=True,
                              name=name)
+    if name == "sliding_window_16k_full":
+        # config 4 without its window: every key for every query, the work the
+        # window's tile bounds save (measured once for contrast)
+        w = make_config(4)
+        w.name = name
+        w.window_left = -1
+        w.window_right = -1
+        return w
     if name == "dense_noncausal_d128":
         return make_workload(seed=2004, ctx_lens=[0, 0], q_lens=[8192, 8192], num_heads=32,
                              num_kv_heads=8, head_size=128, page_size=64, causal=False,
