@@ -172,7 +172,8 @@ def make_launcher(w, cache_only=False, kv_splits=1):
     dev = to_device(w, cache_only=cache_only)
     out = torch.empty_like(dev["q"])
     k = ppa.split_count(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs,
-                        w.total_q_tokens, w.max_q_len, kv_splits)
+                        w.total_q_tokens, w.max_q_len, kv_splits,
+                        window_left=w.window_left, window_right=w.window_right, causal=w.causal)
     need = ppa.workspace_size(w.num_heads, w.head_size, w.total_q_tokens, k)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
     dev["workspace"] = ws
@@ -334,7 +335,8 @@ def run_suite(path, steps, warmup, prewarm_ms=0.0):
         flop = useful_flop(w)
         import paged_kv_prefill_attention_amd as ppa
         k = ppa.split_count(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs,
-                            w.total_q_tokens, w.max_q_len, splits)
+                            w.total_q_tokens, w.max_q_len, splits,
+                            window_left=w.window_left, window_right=w.window_right, causal=w.causal)
         rec = {"config": cid, "workload": w.name, "new_tokens": int(w.q_lens.sum()),
                "kv_splits": k, "requested_splits": splits, "ms_mean": ms,
                "ms_median": per[len(per) // 2],
@@ -364,7 +366,9 @@ def run_tile_sweep(path, steps, warmup, prewarm_ms=0.0):
         prewarm(fn, prewarm_ms)
         ms, per, _ = time_launches(fn, steps, warmup)
         per.sort()
-        bq, bn = ppa.tile_config(w.head_size, w.num_heads, w.num_kv_heads)
+        bq, bn = ppa.tile_config(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs, w.max_q_len,
+                                 window_left=w.window_left, window_right=w.window_right,
+                                 causal=w.causal)
         flop = useful_flop(w)
         rec = {"workload": name, "head_size": w.head_size, "block_q": bq, "block_n": bn,
                "ms_median": per[len(per) // 2], "ms_mean": ms,
@@ -439,7 +443,9 @@ def main():
     value = flop / (ms / 1e3) / 1e12
     achieved = value
     traffic = traffic_from_profiles(w.name)
-    bq, bn = ppa.tile_config(w.head_size, w.num_heads, w.num_kv_heads)
+    bq, bn = ppa.tile_config(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs, w.max_q_len,
+                             window_left=w.window_left, window_right=w.window_right,
+                             causal=w.causal)
     rec = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "prewarm_ms": args.prewarm_ms,

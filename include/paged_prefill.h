@@ -127,15 +127,37 @@ int prefill_attention_validate(const void* q, const void* k_new, const void* v_n
  * prefill_attention_tile_config — the tile geometry prefill_attention uses for this head
  * configuration: *block_q query tokens per Q tile (all heads of a GQA group share a tile) and
  * *block_n keys per KV tile.  The tile bounds below are expressed in these units.  Host-only.
- * The geometry depends on the head configuration only, never on the page size: query rows and
- * KV columns of a tile never index the paged cache, each key is resolved to its page on its own
- * (vLLM PR #54194 report, "Features and motivation", "Implementation breakdown" items 1-2 and
- * "Key source snippets": the tile selection of context_attention_fwd decoupled from pages).  The
- * shapes themselves are chosen per head size by measurement on gfx950, not the report's 128/64.
+ * The geometry never depends on the page size: query rows and KV columns of a tile never index
+ * the paged cache, each key is resolved to its page on its own (vLLM PR #54194 report,
+ * "Features and motivation", "Implementation breakdown" items 1-2 and "Key source snippets":
+ * the tile selection of context_attention_fwd decoupled from pages).  The shapes themselves
+ * are chosen per head size by measurement on gfx950, not the report's 128/64.  At head size 64
+ * block_n also depends on the batch (prefill_attention_tile_config_ex); this form gives the
+ * geometry of a small batch, exact for every other head size.
  * Errors: INVALID_ARG (null outputs, bad head counts), UNSUPPORTED (head_size).
  */
 int prefill_attention_tile_config(int32_t head_size, int32_t num_heads, int32_t num_kv_heads,
                                   int32_t* block_q, int32_t* block_n);
+
+/*
+ * prefill_attention_tile_config_ex — the tile geometry for a batch of num_seqs sequences of at
+ * most max_q_len new tokens under the window (window_left, window_right, causal as for
+ * prefill_attention), as prefill_attention, prefill_attention_tile_bounds and
+ * prefill_attention_kv_splits choose it.  Only head size 64 depends on the batch: with I the
+ * Q-tile work items (num_seqs * cdiv(max_q_len, block_q) per KV head and head block) and S the
+ * workgroups the GPU holds of the 32-key shape (four per CU), block_n is 32 when the window
+ * alone limits a query row to at most 2048 keys (window_left + 1 when causal, window_left + 1
+ * + window_right otherwise) and I >= S, or when I >= 4 S; otherwise block_n is 64.  Multimodal
+ * ranges and the mask options of prefill_attention_ex do not enter the choice.  block_q is the
+ * same either way.  num_seqs = max_q_len = 0 gives prefill_attention_tile_config's answer.
+ * Host-only (it asks the runtime for the current device's CU count).  Errors as for
+ * prefill_attention_tile_config, plus INVALID_ARG for negative sizes, a window below -1 or
+ * causal not 0/1.
+ */
+int prefill_attention_tile_config_ex(int32_t head_size, int32_t num_heads, int32_t num_kv_heads,
+                                     int32_t num_seqs, int32_t max_q_len, int32_t window_left,
+                                     int32_t window_right, int32_t causal, int32_t* block_q,
+                                     int32_t* block_n);
 
 /*
  * prefill_attention_tile_bounds — the KV-tile loop range [lo, hi) of every Q tile, computed on
@@ -145,7 +167,9 @@ int prefill_attention_tile_config(int32_t head_size, int32_t num_heads, int32_t 
  * sequence, and converts to tiles of block_n keys (vLLM PR #50776 report, "Key source
  * snippets"; vLLM PR #53147 report, "Implementation breakdown" item 2).
  *   bounds_out  device int32 [num_seqs][cdiv(max_q_len, block_q)][2], written (lo, hi); tiles
- *               past a sequence's last row get (0, 0).
+ *               past a sequence's last row get (0, 0).  block_q and block_n are those of
+ *               prefill_attention_tile_config_ex(head_size, num_heads, num_kv_heads,
+ *               num_seqs, max_q_len, window_left, window_right, causal).
  * Other arguments as for prefill_attention.  Errors as for prefill_attention.
  */
 int prefill_attention_tile_bounds(const int32_t* query_start_loc, const int32_t* ctx_lens,
@@ -234,24 +258,28 @@ int prefill_attention_ex_noalloc(const void* q, const void* k_new, const void* v
 
 /*
  * prefill_attention_kv_splits — the split count prefill_attention_ex uses for kv_splits,
- * and so the workspace it needs.  kv_splits > 0: kv_splits itself.  kv_splits = 0
- * (automatic), with W the workgroups the GPU runs at once (CUs times the workgroups of this
- * head size that one CU holds: 256 or 1024 on MI355X) and the Q-tile work items bounded from
- * the sizes alone (at most num_seqs * cdiv(max_q_len, block_q) Q tiles, and at most
+ * and so the workspace it needs, for a batch under the window (window_left, window_right,
+ * causal as for prefill_attention; they pick the head-size-64 geometry).  kv_splits > 0:
+ * kv_splits itself.  kv_splits = 0 (automatic), with W the workgroups the GPU runs at once (CUs
+ * times the workgroups that one CU holds of the shape prefill_attention_tile_config_ex names:
+ * 256, 512 or 1024 on MI355X) and the Q-tile work items bounded from the sizes alone (at most
+ * num_seqs * cdiv(max_q_len, block_q) Q tiles, and at most
  * (total_q_tokens + num_seqs * (block_q - 1)) / block_q, times the KV heads):
  *   - a whole number of rounds (a multiple of W, at least W items): 1;
  *   - fewer than 2W items: enough segments for about 2W workgroups, at most 16; every item
- *     longer than its share is cut;
+ *     longer than its share is cut; but 1 when the window alone limits a query row to at
+ *     most 2048 keys (then no item outgrows the share and a split would cut nothing);
  *   - 2W to 4W items whose last round is at most a quarter full (num_seqs <= 256): 4, and
  *     only the items of that last round are cut, by workgroups appended to the grid (the
  *     kernel counts those items exactly from the device-side lengths);
  *   - otherwise 1.
  * Host-only (it asks the runtime for the current device's CU count).  Returns the count
- * (>= 1) or a negative error code (INVALID_ARG for negative sizes or kv_splits outside
- * [0, 64]; UNSUPPORTED as for tile_config).
+ * (>= 1) or a negative error code (INVALID_ARG for negative sizes, kv_splits outside
+ * [0, 64], a window below -1 or causal not 0/1; UNSUPPORTED as for tile_config).
  */
 int prefill_attention_kv_splits(int32_t head_size, int32_t num_heads, int32_t num_kv_heads,
                                 int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                                int32_t window_left, int32_t window_right, int32_t causal,
                                 int32_t kv_splits);
 
 /*

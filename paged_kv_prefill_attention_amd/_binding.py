@@ -37,11 +37,12 @@ _SIGNATURES = {
     "prefill_attention": ([_P] * 8 + [_I] * 7 + [_P, _F, _P] + [_I] * 6 + [_P], _I),
     "prefill_attention_validate": ([_P] * 8 + [_I] * 7 + [_P, _F, _P] + [_I] * 6, _I),
     "prefill_attention_tile_config": ([_I, _I, _I, _P, _P], _I),
+    "prefill_attention_tile_config_ex": ([_I] * 8 + [_P, _P], _I),
     "prefill_attention_tile_bounds": ([_P, _P] + [_I] * 6 + [_P] + [_I] * 3 + [_P, _P], _I),
     "prefill_attention_strerror": ([_I], ctypes.c_char_p),
     "prefill_attention_ex": ([_P] * 8 + [_I] * 7 + [_P, _F, _P] + [_I] * 6
                              + [_P, _I, _I, _I, _I, _P, _U64, _P], _I),
-    "prefill_attention_kv_splits": ([_I] * 7, _I),
+    "prefill_attention_kv_splits": ([_I] * 10, _I),
     "prefill_attention_workspace_size": ([_I] * 4, _U64),
     "prefill_attention_tile_bounds_ex": ([_P, _P] + [_I] * 6 + [_P] + [_I] * 3
                                          + [_P, _I, _I, _I, _P, _P], _I),
@@ -90,13 +91,19 @@ def strerror(code: int) -> str:
     return load_library().prefill_attention_strerror(int(code)).decode()
 
 
-def tile_config(head_size: int, num_heads: int, num_kv_heads: int):
-    """(block_q, block_n): query tokens per Q tile and keys per KV tile."""
+def tile_config(head_size: int, num_heads: int, num_kv_heads: int, num_seqs: int = 0,
+                max_q_len: int = 0, window_left: int = -1, window_right: int = -1,
+                causal: bool = True):
+    """(block_q, block_n): query tokens per Q tile and keys per KV tile, for a batch of
+    ``num_seqs`` sequences of at most ``max_q_len`` new tokens under the given window
+    (0, 0: a small batch; only head size 64 depends on the batch and window)."""
     bq, bn = ctypes.c_int32(), ctypes.c_int32()
-    rc = load_library().prefill_attention_tile_config(head_size, num_heads, num_kv_heads,
-                                                      ctypes.byref(bq), ctypes.byref(bn))
+    rc = load_library().prefill_attention_tile_config_ex(
+        int(head_size), int(num_heads), int(num_kv_heads), int(num_seqs), int(max_q_len),
+        int(window_left), int(window_right), int(bool(causal)), ctypes.byref(bq),
+        ctypes.byref(bn))
     if rc != OK:
-        raise PrefillError(rc, "prefill_attention_tile_config")
+        raise PrefillError(rc, "prefill_attention_tile_config_ex")
     return bq.value, bn.value
 
 
@@ -126,11 +133,13 @@ def _stream(stream):
 
 
 def split_count(head_size: int, num_heads: int, num_kv_heads: int, num_seqs: int,
-                total_q_tokens: int, max_q_len: int, requested: int = 0) -> int:
-    """The split-KV segment count the library uses for ``requested`` (0 = automatic)."""
-    rc = load_library().prefill_attention_kv_splits(head_size, num_heads, num_kv_heads,
-                                                    num_seqs, total_q_tokens, max_q_len,
-                                                    requested)
+                total_q_tokens: int, max_q_len: int, requested: int = 0,
+                window_left: int = -1, window_right: int = -1, causal: bool = True) -> int:
+    """The split-KV segment count the library uses for ``requested`` (0 = automatic) on a
+    batch of these sizes under the given window."""
+    rc = load_library().prefill_attention_kv_splits(
+        int(head_size), int(num_heads), int(num_kv_heads), int(num_seqs), int(total_q_tokens),
+        int(max_q_len), int(window_left), int(window_right), int(bool(causal)), int(requested))
     if rc < 0:
         raise PrefillError(rc, "prefill_attention_kv_splits")
     return rc
@@ -214,7 +223,7 @@ def prefill_attention(q, k_new, v_new, k_cache, v_cache, block_table, query_star
         if rc != OK:
             raise PrefillError(rc, "prefill_attention")
         return out
-    splits = split_count(d, H, Hkv, S, T, mq, int(kv_splits))
+    splits = split_count(d, H, Hkv, S, T, mq, int(kv_splits), window_left, window_right, causal)
     need = workspace_size(H, d, T, splits)
     if need > 0:
         if workspace is None:

@@ -67,9 +67,15 @@ constexpr int kSortMaxSeqs = 256;  // batches up to this size get heavy-first or
 
 // Tile shape per head size: wavefronts per workgroup, keys per KV tile, depth
 // of the LDS ring, wavefronts per SIMD, and 32-row query blocks per wavefront.
-// Overridable at build time (-DPREFILL_TILE_D128=4,64,4,1,2) for sweeps.
+// Overridable at build time (-DPREFILL_TILE_D128=4,64,4,1,2) for sweeps.  Head
+// size 64 has two, picked per call by choose_tiles: PREFILL_TILE_D64 (longer
+// tiles, for long KV loops) and PREFILL_TILE_D64_MANY (more workgroups per CU,
+// shorter tiles, for short windows and batches of many work items).
 #ifndef PREFILL_TILE_D64
-#define PREFILL_TILE_D64 4, 32, 4, 4, 1
+#define PREFILL_TILE_D64 4, 64, 4, 2, 1
+#endif
+#ifndef PREFILL_TILE_D64_MANY
+#define PREFILL_TILE_D64_MANY 4, 32, 4, 4, 1
 #endif
 #ifndef PREFILL_TILE_D128
 #define PREFILL_TILE_D128 8, 64, 4, 2, 1
@@ -480,6 +486,7 @@ struct TileShape {
 };
 template <int D> struct ShapeFor;
 template <> struct ShapeFor<64> { using T = TileShape<64, PREFILL_TILE_D64>; };
+struct ShapeD64Many { using T = TileShape<64, PREFILL_TILE_D64_MANY>; };
 template <> struct ShapeFor<128> { using T = TileShape<128, PREFILL_TILE_D128>; };
 template <> struct ShapeFor<256> { using T = TileShape<256, PREFILL_TILE_D256>; };
 
@@ -1338,6 +1345,7 @@ struct TileChoice {
   int heads_per_tile;
   int block_q;
   int wg_per_cu;  // workgroups resident per CU
+  int many;       // d = 64 only: 1 = the shape for batches of many work items
 };
 
 int gcd_int(int a, int b) {
@@ -1356,7 +1364,41 @@ template <int D> void shape_of(int* rows, int* bn, int* wgs) {
   *wgs = ShapeFor<D>::T::WG_PER_CU;
 }
 
-int choose_tiles(int head_size, int num_heads, int num_kv_heads, TileChoice* tc) {
+int cu_count();
+
+// Keys one query row sees at most when the window alone bounds it (the causal
+// flag closes the right side), else -1.  Multimodal ranges, per-sequence causal
+// flags and chunked masks are not counted: the geometry and split choices that
+// use it are performance rules, and every entry point that needs them has these
+// arguments in common.
+int64_t window_span(int window_left, int window_right, int causal) {
+  if (window_left < 0) return -1;
+  if (causal) return (int64_t)window_left + 1;
+  if (window_right < 0) return -1;
+  return (int64_t)window_left + 1 + window_right;
+}
+
+// A window of at most this many keys per row makes every KV loop short.
+constexpr int64_t kShortSpan = 2048;
+bool short_loops(int window_left, int window_right, int causal) {
+  const int64_t span = window_span(window_left, window_right, causal);
+  return span >= 0 && span <= kShortSpan;
+}
+
+// The tile geometry for a head configuration and, at d = 64, the batch.  Both
+// d = 64 shapes tile the queries alike; the many-items shape (32-key tiles,
+// four workgroups per CU) overlaps each workgroup's prologue, epilogue and
+// memory round trips with three others, while the default shape (64-key tiles,
+// two per CU) halves the per-tile overhead of long KV loops and backfills a
+// second round dynamically.  Measured on gfx950, the many-items shape wins when
+// a short window bounds every loop and the Q-tile items (at most num_seqs *
+// cdiv(max_q_len, block_q) per (KV head, head block) column) fill one round of
+// its slots, or, for loops of any length, from four rounds of items up (at
+// three rounds of long loops it still loses); the default shape wins below
+// that.  num_seqs = max_q_len = 0: the default shape.
+int choose_tiles(int head_size, int num_heads, int num_kv_heads, TileChoice* tc,
+                 int num_seqs = 0, int max_q_len = 0, int window_left = -1,
+                 int window_right = -1, int causal = 1) {
   if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
     return PAGED_PREFILL_ERR_INVALID_ARG;
   if (head_size != 64 && head_size != 128 && head_size != 256)
@@ -1371,6 +1413,20 @@ int choose_tiles(int head_size, int num_heads, int num_kv_heads, TileChoice* tc)
   tc->heads_per_tile = hpt;
   tc->block_q = rows / hpt;
   tc->wg_per_cu = wgs;
+  tc->many = 0;
+  if (head_size == 64 && num_seqs > 0 && max_q_len > 0) {
+    using M = ShapeD64Many::T;
+    static_assert(M::ROWS == ShapeFor<64>::T::ROWS, "both d = 64 shapes tile the queries alike");
+    const int64_t items = (int64_t)num_seqs * ((max_q_len + tc->block_q - 1) / tc->block_q) *
+                          num_kv_heads * (group / hpt);
+    const int64_t slots = (int64_t)cu_count() * M::WG_PER_CU;
+    if ((short_loops(window_left, window_right, causal) && items >= slots) ||
+        items >= 4 * slots) {
+      tc->block_n = M::BN;
+      tc->wg_per_cu = M::WG_PER_CU;
+      tc->many = 1;
+    }
+  }
   return PAGED_PREFILL_OK;
 }
 
@@ -1391,6 +1447,24 @@ struct Options {
 // Device address of `scratch` on the current device, looked up once per device
 // with that device current and kept for every later call.
 constexpr int kMaxDevices = 64;
+std::once_flag g_cu_once[kMaxDevices];
+int g_cu_count[kMaxDevices];
+
+// CUs of the current device, asked once per device (256 on MI355X, and
+// assumed when there is no device to ask).
+int cu_count() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  std::call_once(g_cu_once[dev], [dev] {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    g_cu_count[dev] = cus;
+  });
+  return g_cu_count[dev];
+}
+
 std::once_flag g_scratch_once[kMaxDevices];
 void* g_scratch_ptr[kMaxDevices];
 hipError_t g_scratch_err[kMaxDevices];
@@ -1484,7 +1558,10 @@ int64_t item_slots(int num_seqs, int num_kv_heads, int64_t num_q_tiles, int head
 //  - a whole number of rounds (at least one): no split, there is no partial
 //    round to even out;
 //  - fewer than twice round_slots items: split every long item (the segment-cap
-//    rule), to about 2 * round_slots workgroups, at most 16 segments;
+//    rule), to about 2 * round_slots workgroups, at most 16 segments; but no
+//    split when a short window bounds the loops: the cap (a share of the
+//    longest sequence's tiles) then exceeds every item, so nothing would be cut
+//    and the extra slots and the merge would only cost time;
 //  - two to four rounds of items whose bound leaves a last round at most a
 //    quarter full, for batches whose items the kernel ranks (num_seqs <=
 //    kSortMaxSeqs): tail splitting with kTailSplits segments, which cuts only
@@ -1497,7 +1574,7 @@ struct SplitChoice {
 };
 SplitChoice choose_splits(int kv_splits, int num_seqs, int num_kv_heads, int head_blocks,
                           int64_t num_q_tiles, int total_q_tokens, int block_q,
-                          int round_slots) {
+                          int round_slots, bool short_window) {
   if (kv_splits > 0 || round_slots <= 0) return {kv_splits > 0 ? kv_splits : 1, 0};
   const int64_t tiles = std::min<int64_t>(
       (int64_t)num_seqs * num_q_tiles,
@@ -1505,8 +1582,10 @@ SplitChoice choose_splits(int kv_splits, int num_seqs, int num_kv_heads, int hea
   const int64_t items = tiles * num_kv_heads * head_blocks;
   if (items <= 0) return {1, 0};
   if (items >= round_slots && items % round_slots == 0) return {1, 0};
-  if (items < 2 * (int64_t)round_slots)
+  if (items < 2 * (int64_t)round_slots) {
+    if (short_window) return {1, 0};
     return {(int)std::min<int64_t>(16, (2 * (int64_t)round_slots + items - 1) / items), 0};
+  }
   const int64_t tail = items % round_slots;
   if (num_seqs <= kSortMaxSeqs && items <= 4 * (int64_t)round_slots && tail > 0 &&
       tail <= round_slots / 4)
@@ -1516,14 +1595,7 @@ SplitChoice choose_splits(int kv_splits, int num_seqs, int num_kv_heads, int hea
 
 // Workgroups that run at once: CUs of the current device times the workgroups
 // one CU holds.
-int round_slots_for(const TileChoice& tc) {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    cus = 256;  // MI355X
-  return cus * tc.wg_per_cu;
-}
+int round_slots_for(const TileChoice& tc) { return cu_count() * tc.wg_per_cu; }
 
 uint64_t workspace_bytes_for(int num_heads, int head_size, int total_q_tokens, int splits) {
   if (splits <= 1) return 0;
@@ -1532,9 +1604,9 @@ uint64_t workspace_bytes_for(int num_heads, int head_size, int total_q_tokens, i
   return o_bytes + rows * 2 * sizeof(float);
 }
 
-template <int D>
+template <typename C>
 hipError_t launch(const KernelArgs& a, uint32_t grid, hipStream_t stream) {
-  using C = typename ShapeFor<D>::T;
+  constexpr int D = C::D;
   void* args[] = {(void*)&a};
   hipError_t err = hipLaunchKernel((const void*)&prefill_attention_kernel<C>, dim3(grid),
                                    dim3(C::THREADS), args, 0, stream);
@@ -1569,7 +1641,8 @@ int run(const void* q, const void* k_new, const void* v_new, const void* k_cache
   if (o.kv_splits < 0 || o.kv_splits > kMaxSplits) return PAGED_PREFILL_ERR_INVALID_ARG;
   if (num_seqs == 0 || total_q_tokens == 0 || max_q_len == 0) return PAGED_PREFILL_OK;
   TileChoice tc;
-  rc = choose_tiles(head_size, num_heads, num_kv_heads, &tc);
+  rc = choose_tiles(head_size, num_heads, num_kv_heads, &tc, num_seqs, max_q_len, window_left,
+                    window_right, causal);
   if (rc != PAGED_PREFILL_OK) return rc;
 
   KernelArgs a;
@@ -1610,7 +1683,8 @@ int run(const void* q, const void* k_new, const void* v_new, const void* k_cache
   // the automatic split count needs the device's CU count (one runtime query)
   const int round_slots = o.kv_splits == 0 ? round_slots_for(tc) : 0;
   SplitChoice sc = choose_splits(o.kv_splits, num_seqs, num_kv_heads, a.head_blocks,
-                                 num_q_tiles, total_q_tokens, tc.block_q, round_slots);
+                                 num_q_tiles, total_q_tokens, tc.block_q, round_slots,
+                                 short_loops(window_left, window_right, causal));
   if (o.static_scratch && sc.splits > 1 &&
       workspace_bytes_for(num_heads, head_size, total_q_tokens, sc.splits) > o.workspace_bytes) {
     if (o.kv_splits != 0) return PAGED_PREFILL_ERR_SCRATCH;
@@ -1638,9 +1712,12 @@ int run(const void* q, const void* k_new, const void* v_new, const void* k_cache
   a.main_slots = (int32_t)main_slots;
   hipError_t err;
   switch (head_size) {
-    case 64: err = launch<64>(a, (uint32_t)grid, stream); break;
-    case 128: err = launch<128>(a, (uint32_t)grid, stream); break;
-    default: err = launch<256>(a, (uint32_t)grid, stream); break;
+    case 64:
+      err = tc.many ? launch<ShapeD64Many::T>(a, (uint32_t)grid, stream)
+                    : launch<ShapeFor<64>::T>(a, (uint32_t)grid, stream);
+      break;
+    case 128: err = launch<ShapeFor<128>::T>(a, (uint32_t)grid, stream); break;
+    default: err = launch<ShapeFor<256>::T>(a, (uint32_t)grid, stream); break;
   }
   return err == hipSuccess ? PAGED_PREFILL_OK : PAGED_PREFILL_ERR_HIP;
 }
@@ -1651,7 +1728,8 @@ int run_tile_bounds(const int32_t* query_start_loc, const int32_t* ctx_lens, int
                     int32_t num_seqs, int32_t max_q_len, int32_t max_mm_ranges,
                     const Options& o, int32_t* bounds_out, hipStream_t stream) {
   TileChoice tc;
-  int rc = choose_tiles(head_size, num_heads, num_kv_heads, &tc);
+  int rc = choose_tiles(head_size, num_heads, num_kv_heads, &tc, num_seqs, max_q_len,
+                        window_left, window_right, causal);
   if (rc != PAGED_PREFILL_OK) return rc;
   if (num_seqs < 0 || max_q_len < 0 || max_q_len > kMaxTokens || window_left < -1 ||
       window_right < -1 || (causal != 0 && causal != 1) || max_mm_ranges < 0 ||
@@ -1751,9 +1829,20 @@ int prefill_attention_validate(const void* q, const void* k_new, const void* v_n
 
 int prefill_attention_tile_config(int32_t head_size, int32_t num_heads, int32_t num_kv_heads,
                                   int32_t* block_q, int32_t* block_n) {
-  if (block_q == nullptr || block_n == nullptr) return PAGED_PREFILL_ERR_INVALID_ARG;
+  return prefill_attention_tile_config_ex(head_size, num_heads, num_kv_heads, 0, 0, -1, -1, 1,
+                                          block_q, block_n);
+}
+
+int prefill_attention_tile_config_ex(int32_t head_size, int32_t num_heads, int32_t num_kv_heads,
+                                     int32_t num_seqs, int32_t max_q_len, int32_t window_left,
+                                     int32_t window_right, int32_t causal, int32_t* block_q,
+                                     int32_t* block_n) {
+  if (block_q == nullptr || block_n == nullptr || num_seqs < 0 || max_q_len < 0 ||
+      window_left < -1 || window_right < -1 || (causal != 0 && causal != 1))
+    return PAGED_PREFILL_ERR_INVALID_ARG;
   TileChoice tc;
-  const int rc = choose_tiles(head_size, num_heads, num_kv_heads, &tc);
+  const int rc = choose_tiles(head_size, num_heads, num_kv_heads, &tc, num_seqs, max_q_len,
+                              window_left, window_right, causal);
   if (rc != PAGED_PREFILL_OK) return rc;
   *block_q = tc.block_q;
   *block_n = tc.block_n;
@@ -1830,18 +1919,20 @@ int prefill_attention_ex_noalloc(const void* q, const void* k_new, const void* v
 
 int prefill_attention_kv_splits(int32_t head_size, int32_t num_heads, int32_t num_kv_heads,
                                 int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                                int32_t window_left, int32_t window_right, int32_t causal,
                                 int32_t kv_splits) {
   if (kv_splits < 0 || kv_splits > kMaxSplits || num_seqs < 0 || total_q_tokens < 0 ||
-      max_q_len < 0)
+      max_q_len < 0 || window_left < -1 || window_right < -1 || (causal != 0 && causal != 1))
     return PAGED_PREFILL_ERR_INVALID_ARG;
   TileChoice tc;
-  const int rc = choose_tiles(head_size, num_heads, num_kv_heads, &tc);
+  const int rc = choose_tiles(head_size, num_heads, num_kv_heads, &tc, num_seqs, max_q_len,
+                              window_left, window_right, causal);
   if (rc != PAGED_PREFILL_OK) return rc;
   const int64_t num_q_tiles = ((int64_t)max_q_len + tc.block_q - 1) / tc.block_q;
   return choose_splits(kv_splits, num_seqs, num_kv_heads,
                        num_heads / num_kv_heads / tc.heads_per_tile, num_q_tiles,
-                       total_q_tokens, tc.block_q,
-                       kv_splits == 0 ? round_slots_for(tc) : 0).splits;
+                       total_q_tokens, tc.block_q, kv_splits == 0 ? round_slots_for(tc) : 0,
+                       short_loops(window_left, window_right, causal)).splits;
 }
 
 uint64_t prefill_attention_workspace_size(int32_t num_heads, int32_t head_size,

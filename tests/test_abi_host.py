@@ -95,9 +95,29 @@ def test_invalid_call_returns_before_launch(lib):
 
 
 def test_tile_config(lib):
-    # 8 wavefronts x 32 rows for head sizes 128/256, 4 x 32 rows for 64 (32-key tiles)
+    # 8 wavefronts x 32 rows for head sizes 128/256, 4 x 32 rows for 64
     assert ppa.tile_config(128, 64, 64) == (256, 64)
-    assert ppa.tile_config(64, 8, 8) == (128, 32)
+    assert ppa.tile_config(64, 8, 8) == (128, 64)
+    # d = 64 takes 32-key tiles (four workgroups per CU: 1024 slots on 256 CUs without a GPU to
+    # ask) for four rounds of Q-tile items, or for one round when a window of at most 2048 keys
+    # per row bounds every loop
+    win = dict(window_left=64, window_right=64, causal=False)          # 129 keys per row
+    assert ppa.tile_config(64, 8, 8, 1, 16384) == (128, 64)             # 128 x 8 = 1024 items
+    assert ppa.tile_config(64, 8, 8, 1, 16384, **win) == (128, 32)
+    assert ppa.tile_config(64, 8, 8, 1, 16256, **win) == (128, 64)     # 127 x 8 = 1016 items
+    assert ppa.tile_config(64, 8, 8, 1, 128 * 512) == (128, 32)         # 4096 items
+    assert ppa.tile_config(64, 8, 8, 1, 128 * 512 - 128) == (128, 64)   # 4088 items
+    assert ppa.tile_config(64, 64, 64, 8, 1024) == (128, 32)            # 8 x 8 x 64 = 4096
+    assert ppa.tile_config(64, 16, 8, 4, 512) == (64, 64)               # 4 x 8 x 8 = 256 items
+    assert ppa.tile_config(64, 16, 8, 4, 4096) == (64, 64)              # 2048 items
+    assert ppa.tile_config(64, 16, 8, 4, 4096, 2047, -1, True) == (64, 32)   # 2048 keys
+    assert ppa.tile_config(64, 16, 8, 4, 4096, 2048, -1, True) == (64, 64)   # 2049 keys
+    assert ppa.tile_config(64, 16, 8, 4, 4096, 1023, 1024, False) == (64, 32)  # 2048 keys
+    assert ppa.tile_config(64, 16, 8, 4, 4096, 1023, 1025, False) == (64, 64)
+    assert ppa.tile_config(64, 16, 8, 4, 4096, -1, 10, False) == (64, 64)    # unbounded left
+    assert ppa.tile_config(64, 16, 8, 4, 4096, 100, -1, False) == (64, 64)   # unbounded right
+    assert ppa.tile_config(128, 64, 64, 8, 1024) == (256, 64)   # other head sizes: one shape
+    assert ppa.tile_config(256, 8, 2, 8, 2048, 64, 64, False) == (64, 32)
     assert ppa.tile_config(256, 8, 2) == (64, 32)     # 4 query heads share a tile
     assert ppa.tile_config(256, 16, 8) == (128, 32)
     assert ppa.tile_config(128, 64, 1) == (4, 64)     # MQA: 64 heads x 4 tokens
@@ -165,10 +185,23 @@ def test_split_count_and_workspace_size(lib):
     assert ppa.split_count(256, 8, 2, 8, 10155, 2048, 0) == 2
     # two to four rounds of items with a last round at most a quarter full: tail splitting
     assert ppa.split_count(256, 16, 8, 1, 12454, 12454, 0) == 4   # 784 items, 16 past 3 rounds
-    assert ppa.split_count(64, 8, 8, 1, 33024, 33024, 0) == 4     # 2064 items, 1024 per round
+    # d = 64 without a window: 64-key tiles, 512 per round
+    assert ppa.split_count(64, 8, 8, 1, 33024, 33024, 0) == 1     # 2064 items: past 4 rounds
     assert ppa.split_count(64, 8, 8, 1, 32768, 32768, 0) == 1     # 2048 items: whole rounds
-    assert ppa.split_count(64, 8, 8, 1, 16384, 16384, 0) == 1     # 1024 items: one round
-    assert ppa.split_count(64, 8, 8, 1, 16640, 16640, 0) == 2     # 1040 items: 1 round + 16
+    assert ppa.split_count(64, 8, 8, 1, 16384, 16384, 0) == 1     # 1024 items: whole rounds
+    assert ppa.split_count(64, 8, 8, 1, 16640, 16640, 0) == 4     # 1040 items: 2 rounds + 16
+    # d = 64 under a short window: 32-key tiles, 1024 per round
+    win = dict(window_left=64, window_right=64, causal=False)
+    assert ppa.split_count(64, 8, 8, 1, 33024, 33024, 0, **win) == 4   # 2 rounds + 16
+    assert ppa.split_count(64, 8, 8, 1, 32768, 32768, 0, **win) == 1
+    assert ppa.split_count(64, 8, 8, 1, 16384, 16384, 0, **win) == 1
+    assert ppa.split_count(64, 8, 8, 1, 16640, 16640, 0, **win) == 1   # 1 round + 16: short
+    # fewer than two rounds: long items are split, but not under a short window (2048 keys)
+    assert ppa.split_count(64, 8, 8, 1, 4096, 4096, 0) == 4                  # 256 items
+    assert ppa.split_count(64, 8, 8, 1, 4096, 4096, 0, 2047, -1, True) == 1
+    assert ppa.split_count(64, 8, 8, 1, 4096, 4096, 0, 2048, -1, True) == 4
+    assert ppa.split_count(128, 32, 8, 2, 456, 256, 0, 100, 100, False) == 1
+    assert ppa.split_count(128, 32, 8, 2, 456, 256, 0, -1, 100, False) == 8  # left open
     assert ppa.split_count(256, 8, 2, 8, 1 << 20, 2048, 0) == 1   # 512 items: whole rounds
     assert ppa.split_count(128, 8, 8, 1, 256 * 80, 256 * 80, 0) == 1  # tail of 128: too full
     assert ppa.split_count(128, 64, 64, 8, 1 << 20, 1024, 0) == 1  # 2048 items: no split
@@ -176,6 +209,10 @@ def test_split_count_and_workspace_size(lib):
         ppa.split_count(128, 8, 8, 1, 64, 64, 65)
     with pytest.raises(ppa.PrefillError):
         ppa.split_count(128, 8, 8, 1, -1, 64, 0)
+    with pytest.raises(ppa.PrefillError):
+        ppa.split_count(64, 8, 8, 1, 64, 64, 0, window_left=-2)
+    with pytest.raises(ppa.PrefillError):
+        ppa.tile_config(64, 8, 8, 1, 64, window_left=0, window_right=-2)
     assert ppa.workspace_size(8, 128, 100, 1) == 0
     rows = 3 * 100 * 8
     o_bytes = -(-(rows * 128 * 4) // 256) * 256

@@ -46,7 +46,8 @@ def test_graph_replays_match_eager_bitwise(case, kv_splits):
     print(w.name, "kv_splits", kv_splits, flush=True)
     dev = to_device(w)
     k = ppa.split_count(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs,
-                        w.total_q_tokens, w.max_q_len, kv_splits)
+                        w.total_q_tokens, w.max_q_len, kv_splits,
+                        window_left=w.window_left, window_right=w.window_right, causal=w.causal)
     need = ppa.workspace_size(w.num_heads, w.head_size, w.total_q_tokens, k)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
     out = torch.empty_like(dev["q"])

@@ -29,8 +29,10 @@ def gpu_ready():
 
 
 def tile_q(w):
+    """(block_q, block_n) the library uses for this batch."""
     import paged_kv_prefill_attention_amd as ppa
-    return ppa.tile_config(w.head_size, w.num_heads, w.num_kv_heads)
+    return ppa.tile_config(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs, w.max_q_len,
+                           window_left=w.window_left, window_right=w.window_right, causal=w.causal)
 
 
 def check_sampled(w, out, seed, cache_only=False, mm_ranges="default", rows_per_seq=None):
@@ -85,7 +87,8 @@ def test_config3_automatic_split_sampled():
     import paged_kv_prefill_attention_amd as ppa
     w = make_config(3, page_size=1040)
     k = ppa.split_count(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs,
-                        w.total_q_tokens, w.max_q_len, 0)
+                        w.total_q_tokens, w.max_q_len, 0,
+                        window_left=w.window_left, window_right=w.window_right, causal=w.causal)
     assert k == 2
     out = out_to_f32(run_gpu(w, kv_splits=0))
     err = check_sampled(w, out, seed=33)

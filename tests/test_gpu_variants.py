@@ -88,7 +88,10 @@ def test_variant_tile_bounds_bitexact():
                               causal_per_seq=dev["causal_per_seq"], mm_clamp=w.mm_clamp,
                               chunk_size=w.chunk_size, chunk_lookback=w.chunk_lookback)
         torch.cuda.synchronize()
-        bq, bn = ppa.tile_config(w.head_size, w.num_heads, w.num_kv_heads)
+        bq, bn = ppa.tile_config(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs,
+                                 w.max_q_len,
+                                 window_left=w.window_left, window_right=w.window_right,
+                                 causal=w.causal)
         ref = oracle.tile_bounds_all(w.ctx_lens, w.q_lens, bq, bn, w.causal_arg,
                                      w.window_left, w.window_right, w.mm_ranges,
                                      **w.mask_kwargs())
@@ -115,7 +118,8 @@ def test_split_kv_long_context_short_chunk():
                       num_kv_heads=8, head_size=128, page_size=16, causal=True,
                       name="long_ctx_short_chunk")
     k = ppa.split_count(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs,
-                        w.total_q_tokens, w.max_q_len, 0)
+                        w.total_q_tokens, w.max_q_len, 0,
+                        window_left=w.window_left, window_right=w.window_right, causal=w.causal)
     assert k > 1
     out = out_to_f32(run_gpu(w, kv_splits=0))
     bq, _ = ppa.tile_config(w.head_size, w.num_heads, w.num_kv_heads)
@@ -141,7 +145,9 @@ def test_chunked_local_attention_long_sequence():
         np.array([e - 4096 + o for e in range(4096, 16384, 2048) for o in (-1, 0, 1)
                   if 0 <= e - 4096 + o < 12288])]))
     compare(out[rows], oracle_rows(w, 0, rows), w.name)
-    bq, bn = ppa.tile_config(w.head_size, w.num_heads, w.num_kv_heads)
+    bq, bn = ppa.tile_config(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs, w.max_q_len,
+                             window_left=w.window_left, window_right=w.window_right,
+                             causal=w.causal)
     dev = to_device(w)
     got = ppa.tile_bounds(dev["query_start_loc"], dev["ctx_lens"], w.num_heads, w.num_kv_heads,
                           w.head_size, w.window_left, w.window_right, w.causal,
@@ -227,7 +233,8 @@ def test_tail_splitting_automatic(d, n, causal, wl, wr, note):
                       num_kv_heads=8, head_size=d, page_size=16, causal=causal,
                       window_left=wl, window_right=wr, name="tail_%d_%d" % (d, n))
     print(w.name, note, flush=True)
-    assert ppa.split_count(d, 8, 8, 1, n, n, 0) == 4
+    assert ppa.split_count(d, 8, 8, 1, n, n, 0, window_left=wl, window_right=wr,
+                           causal=causal) == 4
     out = out_to_f32(run_gpu(w, kv_splits=0))
     bq, _ = ppa.tile_config(d, 8, 8)
     first = np.arange(0, 2 * bq)
@@ -243,7 +250,9 @@ def test_tail_splitting_config5():
     from workloads import make_config
     w = make_config(5)
     assert ppa.split_count(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs,
-                           w.total_q_tokens, w.max_q_len, 0) == 4
+                           w.total_q_tokens, w.max_q_len, 0,
+                           window_left=w.window_left, window_right=w.window_right,
+                           causal=w.causal) == 4
     out = out_to_f32(run_gpu(w, kv_splits=0))
     bq, _ = ppa.tile_config(w.head_size, w.num_heads, w.num_kv_heads)
     first = np.arange(0, 2 * bq)

@@ -71,7 +71,8 @@ def test_noalloc_automatic_splits_and_scratch_limit():
     w = make_workload(seed=8103, ctx_lens=[20000], q_lens=[300], num_heads=16, num_kv_heads=4,
                       head_size=128, page_size=1056, causal=True, name="noalloc_auto")
     k = ppa.split_count(w.head_size, w.num_heads, w.num_kv_heads, w.num_seqs, w.total_q_tokens,
-                        w.max_q_len, 0)
+                        w.max_q_len, 0,
+                        window_left=w.window_left, window_right=w.window_right, causal=w.causal)
     assert k > 1 and ppa.workspace_size(w.num_heads, w.head_size, w.total_q_tokens, k) <= SCRATCH
     dev = to_device(w)
     ref = run_gpu(w, dev=dev, kv_splits=0)
@@ -82,7 +83,8 @@ def test_noalloc_automatic_splits_and_scratch_limit():
     # than the scratch: the automatic mode falls back to no split, an explicit count fails
     w5 = make_config(5)
     k5 = ppa.split_count(w5.head_size, w5.num_heads, w5.num_kv_heads, w5.num_seqs,
-                         w5.total_q_tokens, w5.max_q_len, 0)
+                         w5.total_q_tokens, w5.max_q_len, 0,
+                         window_left=w5.window_left, window_right=w5.window_right, causal=w5.causal)
     assert ppa.workspace_size(w5.num_heads, w5.head_size, w5.total_q_tokens, k5) > SCRATCH
     dev5 = to_device(w5)
     plain = run_gpu(w5, dev=dev5)
