@@ -273,17 +273,90 @@ def test_large_batch_without_sequence_sort(d):
     compare(out_to_f32(run_gpu(w)), oracle_full(w), w.name)
 
 
-@pytest.mark.parametrize("d,ctx,page", [(64, 5000, 1), (128, 9000, 1), (64, 7000, 3),
-                                        (64, 480, 1), (64, 560, 1)])
-def test_block_table_beyond_lds_cache(d, ctx, page):
-    """A work item whose KV range covers more pages than the LDS block-table cache
-    holds (512 entries at d=64, 4096 at d=128; the d=64 cases at 480 and 560 cached
-    tokens sit on either side of the limit): pages are read on the scalar unit,
-    with copies that straddle page boundaries and the cache/new-token edge.  Whole
+@pytest.mark.parametrize("d,ctx,page,bn", [(64, 5000, 1, 64), (128, 9000, 1, 64),
+                                           (64, 7000, 3, 64), (64, 2000, 1, 64),
+                                           (64, 2100, 1, 64), (64, 480, 1, 32),
+                                           (64, 560, 1, 32)])
+def test_block_table_beyond_lds_cache(d, ctx, page, bn):
+    """A work item whose cached KV range covers more pages than the LDS block-table
+    cache holds (4096 entries at d=128; at d=64, 2048 for the 64-key shape and 512 for
+    the 32-key one; the cases at 2000/2100 and 480/560 cached tokens sit on either side
+    of those limits): pages are read on the scalar unit, with copies that straddle
+    page boundaries and the cache/new-token edge.  The 32-key cases use a batch of
+    1024 Q-tile items under a 600-key window, which selects that shape.  Whole
     outputs, plain and split-KV."""
-    w = make_workload(seed=4500 + d + page, ctx_lens=[ctx, 40], q_lens=[200, 30],
-                      num_heads=2, num_kv_heads=1, head_size=d, page_size=page, causal=True,
-                      name="bt_fallback_d%d_P%d" % (d, page))
+    if bn == 32:
+        w = make_workload(seed=4600 + ctx, ctx_lens=[ctx, 40], q_lens=[1024, 1024],
+                          num_heads=64, num_kv_heads=64, head_size=d, page_size=page,
+                          causal=True, window_left=600, name="bt_fallback_many_%d" % ctx)
+    else:
+        w = make_workload(seed=4500 + d + page + ctx, ctx_lens=[ctx, 40], q_lens=[200, 30],
+                          num_heads=2, num_kv_heads=1, head_size=d, page_size=page,
+                          causal=True, name="bt_fallback_d%d_P%d_%d" % (d, page, ctx))
+    assert tile_q(w)[1] == bn
     ref = oracle_full(w)
     compare(out_to_f32(run_gpu(w)), ref, w.name)
     compare(out_to_f32(run_gpu(w, kv_splits=3)), ref, w.name + " splits=3")
+
+
+def d64_shape_case(name):
+    """Batches on either side of the d=64 shape rule (32-key tiles for a window of at
+    most 2048 keys per row with at least 1024 Q-tile items, or for 4096 items)."""
+    rng = np.random.default_rng(4700 + len(name))
+    if name == "four_rounds_causal":      # 32 x 8 tiles x 16 KV heads = 4096 items
+        S = 32
+        return make_workload(seed=4701, ctx_lens=rng.integers(0, 400, size=S),
+                             q_lens=rng.integers(900, 1025, size=S), num_heads=16,
+                             num_kv_heads=16, head_size=64, page_size=16, causal=True,
+                             name=name), 32
+    if name == "three_rounds_causal":     # 3072 items: long-loop shape
+        S = 24
+        return make_workload(seed=4702, ctx_lens=rng.integers(0, 400, size=S),
+                             q_lens=rng.integers(900, 1025, size=S), num_heads=16,
+                             num_kv_heads=16, head_size=64, page_size=16, causal=True,
+                             name=name), 64
+    if name == "window_one_round":        # 2 x 64 tiles x 8 = 1024 items, 1501 keys
+        return make_workload(seed=4703, ctx_lens=[300, 0], q_lens=[8192, 8100], num_heads=8,
+                             num_kv_heads=8, head_size=64, page_size=32, causal=True,
+                             window_left=1500, name=name), 32
+    if name == "window_below_round":      # 2 x 63 x 8 = 1008 items
+        return make_workload(seed=4704, ctx_lens=[300, 0], q_lens=[8064, 8000], num_heads=8,
+                             num_kv_heads=8, head_size=64, page_size=32, causal=True,
+                             window_left=1500, name=name), 64
+    if name == "window_past_span":        # 1024 items, 2049 keys per row
+        return make_workload(seed=4705, ctx_lens=[300, 0], q_lens=[8192, 8100], num_heads=8,
+                             num_kv_heads=8, head_size=64, page_size=32, causal=True,
+                             window_left=2048, name=name), 64
+    if name == "bidirectional_window":    # GQA 16/8 (64-token tiles): 2 x 64 x 8 items
+        return make_workload(seed=4706, ctx_lens=[0, 77], q_lens=[4096, 4001], num_heads=16,
+                             num_kv_heads=8, head_size=64, page_size=16, causal=False,
+                             window_left=300, window_right=200, name=name), 32
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("name", ["four_rounds_causal", "three_rounds_causal",
+                                  "window_one_round", "window_below_round",
+                                  "window_past_span", "bidirectional_window"])
+def test_d64_shape_choice(name):
+    """Both d=64 tile shapes on batches at the edges of the rule that picks them: the
+    library reports the expected block_n, and every head of every Q-tile edge row and
+    of random rows matches the oracle, unsplit and under the automatic split count."""
+    w, bn = d64_shape_case(name)
+    assert tile_q(w)[1] == bn, (name, tile_q(w))
+    print(describe_case(w), "block_n", bn, flush=True)
+    dev = to_device(w)
+    plain = out_to_f32(run_gpu(w, dev=dev))
+    auto = out_to_f32(run_gpu(w, dev=dev, kv_splits=0))
+    rng = np.random.default_rng(4710)
+    for s in range(w.num_seqs):
+        rows = edge_rows(w, s, tile_q(w)[0], rng)
+        q0 = int(w.query_start_loc[s])
+        ref = oracle_rows(w, s, rows)
+        compare(plain[q0 + rows], ref, "%s seq %d" % (w.name, s))
+        compare(auto[q0 + rows], ref, "%s seq %d automatic split" % (w.name, s))
+
+
+def describe_case(w):
+    return "%s S=%d H=%d/%d tokens=%d causal=%s window=(%d,%d)" % (
+        w.name, w.num_seqs, w.num_heads, w.num_kv_heads, w.total_q_tokens, w.causal,
+        w.window_left, w.window_right)
