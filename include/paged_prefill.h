@@ -266,9 +266,12 @@ int prefill_attention_ex_noalloc(const void* q, const void* k_new, const void* v
  * num_seqs * cdiv(max_q_len, block_q) Q tiles, and at most
  * (total_q_tokens + num_seqs * (block_q - 1)) / block_q, times the KV heads):
  *   - a whole number of rounds (a multiple of W, at least W items): 1;
- *   - fewer than 2W items: enough segments for about 2W workgroups, at most 16; every item
- *     longer than its share is cut; but 1 when the window alone limits a query row to at
- *     most 2048 keys (then no item outgrows the share and a split would cut nothing);
+ *   - at most W/2 items: k = floor(W / items), one round of segments, or k + 1 when k
+ *     segments per item would leave more than a quarter of the round idle; at most 16;
+ *   - otherwise fewer than 2W items: enough segments for about 2W workgroups, at most 16;
+ *   - in both cases every item longer than its share is cut; but 1 when the window alone
+ *     limits a query row to at most 2048 keys (then no item outgrows the share and a split
+ *     would cut nothing);
  *   - 2W to 4W items whose last round is at most a quarter full (num_seqs <= 256): 4, and
  *     only the items of that last round are cut, by workgroups appended to the grid (the
  *     kernel counts those items exactly from the device-side lengths);

@@ -1557,8 +1557,12 @@ int64_t item_slots(int num_seqs, int num_kv_heads, int64_t num_q_tiles, int head
 // head blocks, that bounds the work items.  Automatic choice:
 //  - a whole number of rounds (at least one): no split, there is no partial
 //    round to even out;
-//  - fewer than twice round_slots items: split every long item (the segment-cap
-//    rule), to about 2 * round_slots workgroups, at most 16 segments; but no
+//  - at most half of round_slots items: split every long item (the segment-cap
+//    rule) into k segments, k * items filling one round (see below), at most
+//    16;
+//  - more than half but fewer than twice round_slots items: split every long
+//    item to about 2 * round_slots workgroups, at most 16 segments; in both
+//    cases no
 //    split when a short window bounds the loops: the cap (a share of the
 //    longest sequence's tiles) then exceeds every item, so nothing would be cut
 //    and the extra slots and the merge would only cost time;
@@ -1584,6 +1588,15 @@ SplitChoice choose_splits(int kv_splits, int num_seqs, int num_kv_heads, int hea
   if (items >= round_slots && items % round_slots == 0) return {1, 0};
   if (items < 2 * (int64_t)round_slots) {
     if (short_window) return {1, 0};
+    if (2 * items <= round_slots) {
+      // At most half a round of items: one round of segments.  Equal items
+      // cut k ways take one segment's time per round, so a partial second
+      // round costs as much as a full one; the largest k that keeps to one
+      // round is taken if it fills at least 3/4 of the slots, else one more.
+      int64_t k = round_slots / items;
+      if (4 * items * k < 3 * (int64_t)round_slots) ++k;
+      return {(int)std::min<int64_t>(16, k), 0};
+    }
     return {(int)std::min<int64_t>(16, (2 * (int64_t)round_slots + items - 1) / items), 0};
   }
   const int64_t tail = items % round_slots;

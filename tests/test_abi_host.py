@@ -178,7 +178,13 @@ def test_split_count_and_workspace_size(lib):
     assert ppa.split_count(128, 64, 64, 8, 3317, 873, 1) == 1
     assert ppa.split_count(128, 64, 64, 8, 3317, 873, 5) == 5
     assert ppa.split_count(128, 64, 64, 8, 3317, 873, 0) == 1   # <= 20 Q tiles x 64 heads
-    assert ppa.split_count(128, 32, 8, 2, 456, 256, 0) == 8     # 2*4 tiles x 8 = 64 items
+    # at most half a round of items (W = 256 at d=128 and 256, 512 for the 64-key d=64
+    # shape without a GPU to ask): k segments per item fill one round, or k + 1 if k
+    # would leave more than a quarter of it idle
+    assert ppa.split_count(128, 32, 8, 2, 456, 256, 0) == 4     # 2*4 tiles x 8 = 64 items
+    assert ppa.split_count(128, 16, 16, 2, 1350, 700, 0) == 2   # 96 items: 192 of 256
+    assert ppa.split_count(256, 8, 2, 4, 2560, 1024, 0) == 3    # 86 items: 172 < 192
+    assert ppa.split_count(64, 16, 8, 1, 512, 512, 0) == 8      # 64 items, W = 512
     assert ppa.split_count(64, 8, 8, 1, 64, 64, 0) == 16        # 8 items, capped at 16
     # the 8-sequence d=256 GQA batch: max_q_len alone allows 8*32 tiles x 2 KV heads = 512
     # items, but 10155 tokens allow at most (10155 + 8*63) / 64 = 166 tiles -> 332 items
@@ -197,11 +203,11 @@ def test_split_count_and_workspace_size(lib):
     assert ppa.split_count(64, 8, 8, 1, 16384, 16384, 0, **win) == 1
     assert ppa.split_count(64, 8, 8, 1, 16640, 16640, 0, **win) == 1   # 1 round + 16: short
     # fewer than two rounds: long items are split, but not under a short window (2048 keys)
-    assert ppa.split_count(64, 8, 8, 1, 4096, 4096, 0) == 4                  # 256 items
+    assert ppa.split_count(64, 8, 8, 1, 4096, 4096, 0) == 2                  # 256 items
     assert ppa.split_count(64, 8, 8, 1, 4096, 4096, 0, 2047, -1, True) == 1
-    assert ppa.split_count(64, 8, 8, 1, 4096, 4096, 0, 2048, -1, True) == 4
+    assert ppa.split_count(64, 8, 8, 1, 4096, 4096, 0, 2048, -1, True) == 2
     assert ppa.split_count(128, 32, 8, 2, 456, 256, 0, 100, 100, False) == 1
-    assert ppa.split_count(128, 32, 8, 2, 456, 256, 0, -1, 100, False) == 8  # left open
+    assert ppa.split_count(128, 32, 8, 2, 456, 256, 0, -1, 100, False) == 4  # left open
     assert ppa.split_count(256, 8, 2, 8, 1 << 20, 2048, 0) == 1   # 512 items: whole rounds
     assert ppa.split_count(128, 8, 8, 1, 256 * 80, 256 * 80, 0) == 1  # tail of 128: too full
     assert ppa.split_count(128, 64, 64, 8, 1 << 20, 1024, 0) == 1  # 2048 items: no split
