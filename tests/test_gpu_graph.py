@@ -37,7 +37,8 @@ def launcher(w, dev, out, kv_splits, workspace):
 
 @pytest.mark.parametrize("case,kv_splits", [(2, 1), (5, 1), (5, 0), (3, 2), (3, 0),
                                             ("long_context_short_chunk", 0),
-                                            ("window_mm_prefix_unclamped", 1)])
+                                            ("window_mm_prefix_unclamped", 1),
+                                            (4, 0), ("sliding_window_16k_full", 0)])
 def test_graph_replays_match_eager_bitwise(case, kv_splits):
     import torch
     import paged_kv_prefill_attention_amd as ppa
